@@ -1,0 +1,212 @@
+// HKV kernels: page summary, two-stage retrieval, active-cache gather.
+//
+// Pages: WorldAttention news summary (ai4snews), HKV paragraph (semantic
+// pages of Psize frames, prompt-level then page-level retrieval of the
+// top-Kp pages) and kernel paragraph (KV reorganisation and contiguous
+// copies are the dominant cost).
+#include "common.h"
+#include "launch.h"
+
+// ---------------------------------------------------------------------------
+// Column sums over a run of token rows. Block = 64 column lanes x 4 token
+// groups; each thread keeps a Kahan sum over its token group, then the four
+// groups are added in a fixed order. Used for the page summary (one page per
+// blockIdx.x) and for the chunk-mean query (one token slab per blockIdx.x).
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_colsum(const T* __restrict__ x, long long rows_per_item, long long item_stride_rows,
+         int rows_per_slab, int HD, float scale, float* __restrict__ out, int out_stride) {
+    const int lane = threadIdx.x & 63;
+    const int grp = threadIdx.x >> 6;
+    const int col = blockIdx.y * 64 + lane;
+    const long long item = blockIdx.x;
+    // rows [r0, r1) of this block
+    long long r0, r1;
+    if (rows_per_slab > 0) {          // slabs of one long run
+        r0 = item * rows_per_slab;
+        r1 = r0 + rows_per_slab;
+        if (r1 > rows_per_item) r1 = rows_per_item;
+    } else {                          // one whole item (a page)
+        r0 = 0;
+        r1 = rows_per_item;
+    }
+    const T* base = x + (rows_per_slab > 0 ? 0 : item * item_stride_rows * HD);
+    Kahan acc;
+    if (col < HD) {
+        for (long long t = r0 + grp; t < r1; t += 4) acc.add(Elt<T>::to_f32(base[t * HD + col]));
+    }
+    __shared__ float part[4][64];
+    part[grp][lane] = acc.s;
+    __syncthreads();
+    if (grp == 0 && col < HD) {
+        float s = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        out[item * out_stride + col] = s * scale;
+    }
+}
+
+template <typename T>
+void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hipStream_t st) {
+    dim3 grid(g.P, (g.HD + 63) / 64);
+    hipLaunchKernelGGL(k_colsum<T>, grid, dim3(256), 0, st, (const T*)pool_k, (long long)g.Tp,
+                       (long long)g.Tp, 0, g.HD, 1.0f / (float)g.Tp, page_kmean, g.HD);
+}
+template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
+template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Retrieval, step 1: partial column sums of q over token slabs.
+
+int retrieve_slabs(const Geo& g) {
+    int slabs = (g.Lq + 63) / 64;
+    return slabs > 64 ? 64 : slabs;
+}
+
+template <typename T>
+void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
+    int slabs = retrieve_slabs(g);
+    int per = (g.Lq + slabs - 1) / slabs;
+    dim3 grid(slabs, (g.HD + 63) / 64);
+    hipLaunchKernelGGL(k_colsum<T>, grid, dim3(256), 0, st, (const T*)q, (long long)g.Lq, 0LL, per,
+                       g.HD, 1.0f, partial, g.HD);
+}
+template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
+template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Retrieval, step 2 (one block of 1024 threads): chunk-mean query, page
+// scores, prompt filter, top-Kp with ties to the lower page, slots ascending.
+
+constexpr int kRetrieveThreads = 1024;
+
+__global__ void __launch_bounds__(kRetrieveThreads)
+k_retrieve(const float* __restrict__ partial, int slabs, int Lq, int HD, int P, int Kp,
+           const float* __restrict__ page_kmean, const int32_t* __restrict__ page_prompt,
+           int cur_prompt, int32_t* __restrict__ page_idx, int32_t* __restrict__ n_sel) {
+    extern __shared__ float smem[];
+    float* qbar = smem;                       // [HD]
+    float* score = smem + HD;                 // [P]
+    int* cand = reinterpret_cast<int*>(score + P);      // [P] 1 if the page matches
+    int* by_rank = cand + P;                  // [64]
+    __shared__ int n_cand;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nwaves = kRetrieveThreads / 64;
+
+    // chunk-mean query, slab partials added in slab order
+    const float inv = 1.0f / (float)Lq;
+    for (int c = tid; c < HD; c += kRetrieveThreads) {
+        float s = 0.f;
+        for (int k = 0; k < slabs; ++k) s += partial[(size_t)k * HD + c];
+        qbar[c] = s * inv;
+    }
+    if (tid == 0) n_cand = 0;
+    if (tid < 64) by_rank[tid] = -1;
+    __syncthreads();
+
+    // page scores, one wave per page; fixed lane order and a fixed tree
+    for (int p = wave; p < P; p += nwaves) {
+        const bool match = page_prompt[p] == cur_prompt;
+        float s = 0.f;
+        if (match) {
+            const float* km = page_kmean + (size_t)p * HD;
+            for (int c = lane; c < HD; c += 64) s = fmaf(km[c], qbar[c], s);
+            s = wave_sum(s);
+        }
+        if (lane == 0) {
+            score[p] = s;
+            cand[p] = match ? 1 : 0;
+            if (match) atomicAdd(&n_cand, 1);
+        }
+    }
+    __syncthreads();
+
+    // rank of each candidate: better score, or equal score and lower index
+    for (int p = tid; p < P; p += kRetrieveThreads) {
+        if (!cand[p]) continue;
+        const float sp = score[p];
+        int rank = 0;
+        for (int o = 0; o < P && rank < Kp; ++o) {
+            if (!cand[o] || o == p) continue;
+            const float so = score[o];
+            if (so > sp || (so == sp && o < p)) ++rank;
+        }
+        if (rank < Kp) by_rank[rank] = p;
+    }
+    __syncthreads();
+
+    if (tid == 0) {
+        int n = n_cand < Kp ? n_cand : Kp;
+        int chosen[64];
+        for (int k = 0; k < n; ++k) chosen[k] = by_rank[k];
+        for (int a = 1; a < n; ++a) {            // insertion sort, ascending page index
+            int v = chosen[a], b = a - 1;
+            while (b >= 0 && chosen[b] > v) { chosen[b + 1] = chosen[b]; --b; }
+            chosen[b + 1] = v;
+        }
+        for (int k = 0; k < Kp; ++k) page_idx[k] = k < n ? chosen[k] : -1;
+        *n_sel = n;
+    }
+}
+
+size_t retrieve_smem_bytes(const Geo& g) {
+    return (size_t)g.HD * 4 + (size_t)g.P * 8 + 64 * 4;
+}
+
+void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
+                     const int32_t* page_prompt, int cur_prompt, int32_t* page_idx,
+                     int32_t* n_sel, hipStream_t st) {
+    hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st,
+                       partial, retrieve_slabs(g), g.Lq, g.HD, g.P, g.Kp, page_kmean, page_prompt,
+                       cur_prompt, page_idx, n_sel);
+}
+
+// ---------------------------------------------------------------------------
+// Gather: slot s of the active cache <- pool page page_idx[s], for K and V.
+// A pure HBM-to-HBM copy: 16-byte vectors, kGatherUnroll loads in flight per
+// thread before the stores. blockIdx.y = slot, blockIdx.z = 0 for K, 1 for V.
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 8;
+
+__global__ void __launch_bounds__(kGatherThreads)
+k_gather(const u32x4* __restrict__ pool_k, const u32x4* __restrict__ pool_v,
+         const int32_t* __restrict__ page_idx, const int32_t* __restrict__ n_sel,
+         u32x4* __restrict__ k_hist, u32x4* __restrict__ v_hist, long long vec_per_page) {
+    const int slot = blockIdx.y;
+    if (slot >= *n_sel) return;
+    const long long page = page_idx[slot];
+    const u32x4* src = (blockIdx.z == 0 ? pool_k : pool_v) + page * vec_per_page;
+    u32x4* dst = (blockIdx.z == 0 ? k_hist : v_hist) + (long long)slot * vec_per_page;
+    const long long chunk = (long long)kGatherThreads * kGatherUnroll;
+    for (long long base = (long long)blockIdx.x * chunk; base < vec_per_page;
+         base += (long long)gridDim.x * chunk) {
+        u32x4 v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            long long i = base + u * kGatherThreads + threadIdx.x;
+            if (i < vec_per_page) v[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            long long i = base + u * kGatherThreads + threadIdx.x;
+            if (i < vec_per_page) dst[i] = v[u];
+        }
+    }
+}
+
+void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* pool_v,
+                   const int32_t* page_idx, const int32_t* n_sel, void* k_hist, void* v_hist,
+                   hipStream_t st) {
+    long long vec = (long long)g.Tp * g.HD * elt_bytes / 16;
+    long long chunk = (long long)kGatherThreads * kGatherUnroll;
+    long long blocks = (vec + chunk - 1) / chunk;
+    if (blocks > 4096) blocks = 4096;
+    dim3 grid((unsigned)blocks, g.Kp, 2);
+    hipLaunchKernelGGL(k_gather, grid, dim3(kGatherThreads), 0, st, (const u32x4*)pool_k,
+                       (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec);
+}

@@ -1,0 +1,55 @@
+// Internal launchers of libhsakv (not exported). Each enqueues on `st` and
+// returns immediately; the caller checks hipGetLastError.
+#pragma once
+
+#include "common.h"
+
+// Epilogue of the attention kernels.
+//  o_main : f32 [Lq][H][d] receives O (NULL: not written)
+//  out    : dtype [Lq][H][d] receives the gated fusion g*O + (1-g)*o_lin (NULL: no fusion)
+//  o_lin  : f32 [Lq][H][d] the low-rank branch, read when `out` is set
+//  gate   : f32 [Lq][H] receives g (NULL: not written); only with `out`
+//  w_g, b_g : gate parameters, read when `out` is set
+struct Epi {
+    float* o_main;
+    void* out;
+    const float* o_lin;
+    float* gate;
+    const float* w_g;
+    const float* b_g;
+};
+
+template <typename T> void launch_page_summary(const Geo&, const void* pool_k, float* page_kmean, hipStream_t);
+int retrieve_slabs(const Geo&);
+size_t retrieve_smem_bytes(const Geo&);
+template <typename T> void launch_q_partials(const Geo&, const void* q, float* partial, hipStream_t);
+void launch_retrieve(const Geo&, const float* partial, const float* page_kmean, const int32_t* page_prompt,
+                     int cur_prompt, int32_t* page_idx, int32_t* n_sel, hipStream_t);
+void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* pool_v, const int32_t* page_idx,
+                   const int32_t* n_sel, void* k_hist, void* v_hist, hipStream_t);
+
+template <typename T>
+void launch_pool(const Geo&, const void* q, const void* k_hist, const void* k_intra, const int32_t* n_sel,
+                 float* qb, float* kb, hipStream_t);
+void launch_select(const Geo&, const float* qb, const float* kb, const int32_t* n_sel, const TauArg& tau,
+                   int32_t* sel_count, int32_t* sel_idx, uint8_t* sel_mask, float* block_mass, hipStream_t);
+
+template <typename T>
+void launch_sparse_attn(const Geo&, const void* q, const void* k_hist, const void* v_hist, const void* k_intra,
+                        const void* v_intra, const int32_t* n_sel, const int32_t* sel_count,
+                        const int32_t* sel_idx, const int32_t* row_order, const Epi& ep, hipStream_t);
+template <typename T>
+void launch_lowrank_attn(const Geo&, const void* q, const void* k_hi, const void* v_hi, const void* k_lo,
+                         const void* v_lo, const Epi& ep, hipStream_t);
+
+int lowrank_splits(const Geo&);
+template <typename T>
+void launch_lowrank_proj(const Geo&, const void* E, const void* F, const void* k_hist, const void* v_hist,
+                         const void* k_intra, const void* v_intra, const int32_t* n_sel, float* part,
+                         hipStream_t);
+template <typename T>
+void launch_lowrank_reduce(const Geo&, const float* part, float* k_low, float* v_low, void* k_hi, void* v_hi,
+                           void* k_lo, void* v_lo, hipStream_t);
+template <typename T>
+void launch_fuse(const Geo&, const void* q, const float* w_g, const float* b_g, const float* o_s,
+                 const float* o_l, void* out, float* gate, hipStream_t);
