@@ -73,6 +73,11 @@ template <> struct Elt<bf16_t> {
     HSAKV_DEV static bf16_t from_f32(float v) { return f32_to_bf16(v); }
 };
 
+// 2^x with the hardware v_exp_f32 alone. Results below 2^-126 flush to zero
+// instead of going through the denormal fix-up: softmax weights that small
+// vanish against the row sum, so the probabilities are unchanged.
+HSAKV_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Wave-level helpers (64 lanes).
 HSAKV_DEV float wave_sum(float v) {
 #pragma unroll

@@ -198,14 +198,14 @@ HSAKV_DEV void tile_step(WaveState<T, D>& ws, const Tile<T, D>& th, const Tile<T
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(ws.m, mx);
-    const float alpha = exp2f(ws.m - m_new);   // m starts at -inf: exp2(-inf) = 0
+    const float alpha = fast_exp2(ws.m - m_new);   // m starts at -inf: exp2(-inf) = 0
     ws.m = m_new;
     float rs = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float p = exp2f(s[t][j] - m_new);
+            const float p = fast_exp2(s[t][j] - m_new);
             s[t][j] = p;
             rs += p;
         }
@@ -402,6 +402,12 @@ void launch_sparse_attn(const Geo& g, const void* q, const void* k_hist, const v
                         const void* k_intra, const void* v_intra, const int32_t* n_sel,
                         const int32_t* sel_count, const int32_t* sel_idx,
                         const int32_t* row_order, const Epi& ep, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {
+        // bf16: the 32x32x16 MFMA kernel with transpose reads (k_sparse32.hip)
+        launch_sparse_attn_bf16_mfma32(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
+                                       sel_idx, ep, st);
+        return;
+    }
     dim3 grid(g.H * g.NQB);
     if (g.d == 128)
         hipLaunchKernelGGL((k_sparse_attn<T, 128>), grid, dim3(kAttnThreads), 0, st, g, (const T*)q,
