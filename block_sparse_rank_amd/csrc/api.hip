@@ -39,6 +39,7 @@ Geo make_geo(const hsakv_dims* d) {
     g.NBh_max = (int)((g.hist_rows + d->Binter - 1) / d->Binter);
     g.NB_max = g.NBh_max + g.NBc;
     g.L = g.hist_rows + d->Lq;
+    g.elt = d->dtype == HSAKV_BF16 ? 2 : 4;
     return g;
 }
 
@@ -83,7 +84,7 @@ int done() {
 
 // ---- workspace sizes -------------------------------------------------------
 
-size_t ws_gather(const Geo& g) { return align_up((size_t)retrieve_slabs(g) * g.HD * 4); }
+size_t ws_gather(const Geo& g) { return align_up(((size_t)retrieve_slabs(g) + 1) * g.HD * 4); }
 
 size_t ws_select(const Geo& g) {
     return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4);

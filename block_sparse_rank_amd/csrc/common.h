@@ -22,6 +22,7 @@ struct Geo {
     int NB_max;    // NBh_max + NBc
     long long hist_rows;  // Kp * Tp
     long long L;          // Kp * Tp + Lq: columns of E and F
+    int elt;              // bytes per element of the storage type (2 bf16, 4 f32)
 };
 
 // Per-head thresholds passed by value in the kernel arguments, so no host to

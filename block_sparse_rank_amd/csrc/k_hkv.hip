@@ -74,13 +74,30 @@ template void launch_q_partials<float>(const Geo&, const void*, float*, hipStrea
 template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
-// Retrieval, step 2 (one block of 1024 threads): chunk-mean query, page
-// scores, prompt filter, top-Kp with ties to the lower page, slots ascending.
+// Retrieval, step 2: chunk-mean query, one column per thread, slab partials
+// added in slab order.
+
+__global__ void __launch_bounds__(256)
+k_qbar(const float* __restrict__ partial, int slabs, int HD, float inv_Lq, float* __restrict__ qbar) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= HD) return;
+    float v[64];
+#pragma unroll
+    for (int k = 0; k < 64; ++k) v[k] = k < slabs ? partial[(size_t)k * HD + c] : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) s += v[k];
+    qbar[c] = s * inv_Lq;
+}
+
+// ---------------------------------------------------------------------------
+// Retrieval, step 3 (one block of 1024 threads): page scores, prompt filter,
+// top-Kp with ties to the lower page, slots ascending.
 
 constexpr int kRetrieveThreads = 1024;
 
 __global__ void __launch_bounds__(kRetrieveThreads)
-k_retrieve(const float* __restrict__ partial, int slabs, int Lq, int HD, int P, int Kp,
+k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
            const float* __restrict__ page_kmean, const int32_t* __restrict__ page_prompt,
            int cur_prompt, int32_t* __restrict__ page_idx, int32_t* __restrict__ n_sel) {
     extern __shared__ float smem[];
@@ -95,24 +112,27 @@ k_retrieve(const float* __restrict__ partial, int slabs, int Lq, int HD, int P, 
     const int wave = tid >> 6;
     const int nwaves = kRetrieveThreads / 64;
 
-    // chunk-mean query, slab partials added in slab order
-    const float inv = 1.0f / (float)Lq;
-    for (int c = tid; c < HD; c += kRetrieveThreads) {
-        float s = 0.f;
-        for (int k = 0; k < slabs; ++k) s += partial[(size_t)k * HD + c];
-        qbar[c] = s * inv;
-    }
+    for (int c = tid; c < HD; c += kRetrieveThreads) qbar[c] = qbar_g[c];
     if (tid == 0) n_cand = 0;
     if (tid < 64) by_rank[tid] = -1;
     __syncthreads();
 
-    // page scores, one wave per page; fixed lane order and a fixed tree
+    // page scores, one wave per page; lanes take columns lane, lane + 64, ...
+    // in a fixed order (eight independent loads in flight), then a fixed tree
     for (int p = wave; p < P; p += nwaves) {
         const bool match = page_prompt[p] == cur_prompt;
         float s = 0.f;
         if (match) {
             const float* km = page_kmean + (size_t)p * HD;
-            for (int c = lane; c < HD; c += 64) s = fmaf(km[c], qbar[c], s);
+            int c = lane;
+            for (; c + 7 * 64 < HD; c += 8 * 64) {
+                float k8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) k8[u] = km[c + 64 * u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s = fmaf(k8[u], qbar[c + 64 * u], s);
+            }
+            for (; c < HD; c += 64) s = fmaf(km[c], qbar[c], s);
             s = wave_sum(s);
         }
         if (lane == 0) {
@@ -158,9 +178,13 @@ size_t retrieve_smem_bytes(const Geo& g) {
 void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
                      const int32_t* page_prompt, int cur_prompt, int32_t* page_idx,
                      int32_t* n_sel, hipStream_t st) {
+    // the chunk mean goes right after the slab partials in the workspace
+    float* qbar = const_cast<float*>(partial) + (size_t)retrieve_slabs(g) * g.HD;
+    hipLaunchKernelGGL(k_qbar, dim3((g.HD + 255) / 256), dim3(256), 0, st, partial,
+                       retrieve_slabs(g), g.HD, 1.0f / (float)g.Lq, qbar);
     hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st,
-                       partial, retrieve_slabs(g), g.Lq, g.HD, g.P, g.Kp, page_kmean, page_prompt,
-                       cur_prompt, page_idx, n_sel);
+                       (const float*)qbar, g.HD, g.P, g.Kp, page_kmean, page_prompt, cur_prompt,
+                       page_idx, n_sel);
 }
 
 // ---------------------------------------------------------------------------

@@ -202,6 +202,7 @@ k_fuse(Geo g, const T* __restrict__ q, const float* __restrict__ w_g, const floa
 }  // namespace
 
 int lowrank_splits(const Geo& g) {
+    if (proj32_eligible(g)) return proj32_splits(g);
     const int tiles = ((g.HD + PBN - 1) / PBN) * ((g.r + PBM - 1) / PBM) * 2;
     int s = (512 + tiles - 1) / tiles;
     if (s < 1) s = 1;
@@ -213,6 +214,10 @@ template <typename T>
 void launch_lowrank_proj(const Geo& g, const void* E, const void* F, const void* k_hist,
                          const void* v_hist, const void* k_intra, const void* v_intra,
                          const int32_t* n_sel, float* part, hipStream_t st) {
+    if (sizeof(T) == 2 && proj32_eligible(g)) {
+        launch_lowrank_proj32(g, E, F, k_hist, v_hist, k_intra, v_intra, n_sel, part, st);
+        return;
+    }
     const int ns = lowrank_splits(g);
     dim3 grid((g.HD + PBN - 1) / PBN, (g.r + PBM - 1) / PBM, ns * 2);
     hipLaunchKernelGGL(k_lowrank_proj<T>, grid, dim3(kProjThreads), 0, st, g, (const T*)E,

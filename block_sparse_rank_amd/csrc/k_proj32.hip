@@ -1,0 +1,270 @@
+// Low-rank projection K' = E K_act, V' = F V_act in bf16 on gfx950 32x32x16 MFMA.
+//
+// Pages: WorldAttention news summary (ai4snews), HSA paragraph (a
+// Linformer-style low-rank global branch, O(L r)); the projection is the
+// Linformer paper's (cited on the mlsanity map): one E and one F of shape
+// [r][L] shared by every head, applied to the keys and values of the active
+// cache followed by the chunk.
+//
+// As a GEMM: C[m][n] = sum_k X[m][col(k)] Y[k][n] with X = E or F (rows of r,
+// k-contiguous), Y = the active keys or values as [L_act][H*d] (n-contiguous)
+// and k running over the present history rows then the chunk rows. It is a
+// long-K contraction (K = 54600 at the 1.3B 480p shape) with a small output
+// (r x H*d), so it is split along k; each split writes an f32 partial and a
+// separate pass adds the partials in split order.
+//
+// Work-group = 8 waves, tile 256 (m) x 128 (n), k-step 64. Wave w computes
+// rows 64(w%4).. and columns 64(w/4).. with four 32x32 accumulators. Tiles
+// are brought into LDS by global -> LDS DMA (two buffers, the next k-step in
+// flight during the MFMA work). DMA writes 64 lanes x 16 bytes contiguously,
+// so the padded row pitch that keeps the operand reads free of bank conflicts
+// is made by "pad lanes": the X tile has 9 slots per row (8 data + 1 pad,
+// 144 B pitch), the Y tile 18 (16 + 2, 288 B pitch); a pad lane loads any
+// valid address and lands in the pad. X fragments are ds_read_b128 rows; Y
+// fragments come from ds_read_b64_tr_b16 transpose reads of the row-major
+// tile (lane i of a 16-lane group receives column c0 + i of four rows).
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int BM = 256, BN = 128, BK = 64, NT = 512, NWV = 8;
+constexpr int A_SLOTS = BK / 8 + 1;           // 9
+constexpr int B_SLOTS = BN / 8 + 2;           // 18
+constexpr int A_ROWB = A_SLOTS * 16;          // 144
+constexpr int B_ROWB = B_SLOTS * 16;          // 288
+constexpr int A_BYTES = BM * A_ROWB;          // 36864
+constexpr int B_BYTES = BK * B_ROWB;          // 18432
+constexpr int STAGE = A_BYTES + B_BYTES;      // 55296; two stages: 110592 bytes
+constexpr int A_INSTR = BM * A_SLOTS / 64;    // 36
+constexpr int B_INSTR = BK * B_SLOTS / 64;    // 18
+static_assert(BM * A_SLOTS % 64 == 0 && BK * B_SLOTS % 64 == 0, "whole wave instructions");
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+HSAKV_DEV void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+struct ProjArgs {
+    const bf16_t* X;      // E or F
+    const bf16_t* Yh;     // k_hist or v_hist
+    const bf16_t* Yc;     // k_intra or v_intra
+    long long Lh;         // present history rows
+    long long Lact;       // Lh + Lq
+};
+
+// Per-lane DMA offsets that do not change from one k-step to the next: the
+// X row (clamped to r) and k slot, the Y row and n slot of each of this wave's
+// instructions (at most A_PER / B_PER of them).
+constexpr int A_PER = (A_INSTR + NWV - 1) / NWV;
+constexpr int B_PER = (B_INSTR + NWV - 1) / NWV;
+struct DmaLanes {
+    int a_off[A_PER];    // m * L + 8 * slot (slot 0 for the pad lane)
+    int b_row[B_PER];    // k row inside the stage
+    int b_col[B_PER];    // n0 + 8 * slot
+};
+
+HSAKV_DEV void dma_lanes(DmaLanes& dl, const Geo& g, int m0, int n0) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+        const int L = (wave + NWV * q) * 64 + lane;
+        const int row = L / A_SLOTS, sl = L % A_SLOTS;
+        int m = m0 + row;
+        m = m < g.r ? m : g.r - 1;
+        dl.a_off[q] = m * (int)g.L + (sl < BK / 8 ? sl : 0) * 8;
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+        const int L = (wave + NWV * q) * 64 + lane;
+        const int row = L / B_SLOTS, sl = L % B_SLOTS;
+        dl.b_row[q] = row;
+        dl.b_col[q] = n0 + (sl < BN / 8 ? sl : 0) * 8;
+    }
+}
+
+// DMA one k-step (X: 256 rows x 64 k; Y: 64 k rows x 128 n) into `buf`.
+// Fast path: the step lies on one side of the history/chunk seam and inside
+// the split, so every address is a uniform base plus a fixed lane offset.
+// Otherwise each lane maps its own k: k past the valid range reads a clamped
+// (valid) address, and the Y rows past the split's end are zeroed before use.
+HSAKV_DEV void dma_stage(char* buf, const Geo& g, const ProjArgs& a, const DmaLanes& dl, long long k0,
+                         long long ke) {
+    const int wave = threadIdx.x >> 6;
+    const bool fast = k0 + BK <= ke && (k0 + BK <= a.Lh || k0 >= a.Lh);
+    if (fast) {
+        const bool hist = k0 < a.Lh;
+        const bf16_t* xb = a.X + (hist ? k0 : g.hist_rows + (k0 - a.Lh));
+        const bf16_t* yb = hist ? a.Yh + k0 * g.HD : a.Yc + (k0 - a.Lh) * g.HD;
+#pragma unroll
+        for (int q = 0; q < A_PER; ++q) {
+            const int j = wave + NWV * q;
+            if (j < A_INSTR)
+                __builtin_amdgcn_global_load_lds(xb + dl.a_off[q], (lds_void_t*)(buf + j * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < B_PER; ++q) {
+            const int j = wave + NWV * q;
+            if (j < B_INSTR)
+                __builtin_amdgcn_global_load_lds(yb + dl.b_row[q] * g.HD + dl.b_col[q],
+                                                 (lds_void_t*)(buf + A_BYTES + j * 1024), 16, 0, 0);
+        }
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < A_PER; ++q) {
+        const int j = wave + NWV * q;
+        if (j >= A_INSTR) continue;
+        const int L = j * 64 + lane;
+        const int sl = L % A_SLOTS;
+        long long k = k0 + (sl < BK / 8 ? sl : 0) * 8;
+        k = k + 8 <= a.Lact ? k : a.Lact - 8;
+        const long long col = k < a.Lh ? k : g.hist_rows + (k - a.Lh);
+        const int mrow = dl.a_off[q] / (int)g.L;
+        __builtin_amdgcn_global_load_lds(a.X + (long long)mrow * g.L + col, (lds_void_t*)(buf + j * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < B_PER; ++q) {
+        const int j = wave + NWV * q;
+        if (j >= B_INSTR) continue;
+        long long k = k0 + dl.b_row[q];
+        k = k < a.Lact ? k : a.Lact - 1;
+        const bf16_t* src = (k < a.Lh ? a.Yh + k * g.HD : a.Yc + (k - a.Lh) * g.HD) + dl.b_col[q];
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + A_BYTES + j * 1024), 16, 0, 0);
+    }
+}
+
+// Zero the Y rows [first, BK) of a stage (the k past the split's end).
+HSAKV_DEV void zero_tail(char* buf, int first) {
+    for (int idx = threadIdx.x; idx < (BK - first) * (BN / 8); idx += NT) {
+        const int row = first + idx / (BN / 8), c = idx % (BN / 8);
+        *reinterpret_cast<uint4*>(buf + A_BYTES + row * B_ROWB + c * 16) = uint4{0, 0, 0, 0};
+    }
+}
+
+HSAKV_DEV void compute_stage(const char* buf, f32x16_t (&acc)[2][2]) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int mw = wave & 3, nw = wave >> 2;
+    const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
+    const char* A = buf;
+    const char* B = buf + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8_t af[2], bfr[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            af[mt] = *reinterpret_cast<const bf16x8_t*>(A + (64 * mw + 32 * mt + r32) * A_ROWB + (16 * ks + 8 * g2) * 2);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int krow = 16 * ks + 8 * (G >> 1) + (j >> 2);
+            const int col = 64 * nw + 32 * nt + 16 * (G & 1) + 4 * (j & 3);
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(B + krow * B_ROWB + col * 2));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(B + (krow + 4) * B_ROWB + col * 2));
+            bfr[nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+    }
+}
+
+__global__ void __launch_bounds__(NT, 1)
+k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__ F,
+                 const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+                 const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
+                 const int32_t* __restrict__ n_sel_p, int nsplit, int per_xcd, float* __restrict__ part) {
+    // two distinct LDS objects with fixed roles per step, so the compiler can
+    // tell the next step's DMA from this step's reads
+    __shared__ __attribute__((aligned(16))) char buf0[STAGE];
+    __shared__ __attribute__((aligned(16))) char buf1[STAGE];
+    const int MT = (g.r + BM - 1) / BM, NTL = g.HD / BN;
+    const int total = nsplit * 2 * MT * NTL;
+    const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (lin >= total) return;
+    const int nt_i = lin % NTL;
+    const int mt_i = (lin / NTL) % MT;
+    const int z = (lin / (NTL * MT)) & 1;
+    const int split = lin / (NTL * MT * 2);
+    const int m0 = mt_i * BM, n0 = nt_i * BN;
+    ProjArgs a;
+    a.X = z ? F : E;
+    a.Yh = z ? v_hist : k_hist;
+    a.Yc = z ? v_intra : k_intra;
+    a.Lh = (long long)(*n_sel_p) * g.Tp;
+    a.Lact = a.Lh + g.Lq;
+    const long long per = ((g.L + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+    const long long kb = (long long)split * per;
+    const long long ke = kb + per < a.Lact ? kb + per : a.Lact;
+    DmaLanes dl;
+    dma_lanes(dl, g, m0, n0);
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16_t{};
+
+    long long k0 = kb;
+    if (k0 < ke) dma_stage(buf0, g, a, dl, k0, ke);
+    auto step = [&](char* now, char* nxt) __attribute__((always_inline)) {
+        wait_vmcnt0();
+        __syncthreads();
+        if (k0 + BK > ke) {                  // last, partial k-step of the split
+            zero_tail(now, (int)(ke - k0));
+            __syncthreads();
+        }
+        if (k0 + BK < ke) dma_stage(nxt, g, a, dl, k0 + BK, ke);
+        compute_stage(now, acc);
+        k0 += BK;
+    };
+    while (k0 < ke) {
+        step(buf0, buf1);
+        if (k0 >= ke) break;
+        step(buf1, buf0);
+    }
+
+    // D[m = 8(i/4) + 4(l/32) + i%4][n = l%32] of each 32x32 accumulator
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int mw = wave & 3, nw = wave >> 2, g2 = lane >> 5;
+    float* out = part + (size_t)(split * 2 + z) * g.r * g.HD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + 64 * mw + 32 * mt + 8 * (i >> 2) + 4 * g2 + (i & 3);
+                const int n = n0 + 64 * nw + 32 * nt + (lane & 31);
+                if (m < g.r) out[(size_t)m * g.HD + n] = acc[mt][nt][i];
+            }
+}
+
+}  // namespace
+
+// The MFMA projection needs 16-byte aligned 8-element runs of E's columns
+// and of the key rows on both sides of the history/chunk seam.
+bool proj32_eligible(const Geo& g) {
+    return g.elt == 2 && g.Tp % 8 == 0 && g.Lq % 8 == 0 && g.L % 8 == 0 && g.HD % BN == 0;
+}
+
+int proj32_splits(const Geo& g) {
+    const int tiles = 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
+    int s = (256 + tiles - 1) / tiles;
+    return s < 1 ? 1 : (s > 32 ? 32 : s);
+}
+
+void launch_lowrank_proj32(const Geo& g, const void* E, const void* F, const void* k_hist,
+                           const void* v_hist, const void* k_intra, const void* v_intra,
+                           const int32_t* n_sel, float* part, hipStream_t st) {
+    const int ns = proj32_splits(g);
+    const int total = ns * 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
+    const int per_xcd = (total + 7) / 8;
+    hipLaunchKernelGGL(k_lowrank_proj32, dim3(8 * per_xcd), dim3(NT), 0, st, g, (const bf16_t*)E,
+                       (const bf16_t*)F, (const bf16_t*)k_hist, (const bf16_t*)v_hist,
+                       (const bf16_t*)k_intra, (const bf16_t*)v_intra, n_sel, ns, per_xcd, part);
+}

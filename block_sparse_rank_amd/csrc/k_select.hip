@@ -266,9 +266,151 @@ k_select(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
     if (tid == 0) sel_count[(size_t)h * g.NQB + i] = kstar;
 }
 
+// ---------------------------------------------------------------------------
+// Selection, one wave per row, everything in registers (NB <= 64 * NPL).
+// Lane l owns blocks b = l + 64 j. After the softmax, the selected set is the
+// shortest prefix of the order (mass descending, id ascending) whose mass
+// reaches tau. With key(b) = (~bits(p_b), b) (ascending key = that order) it
+// is {b : key(b) <= K*}, K* the smallest key with S(K) >= tau, where
+// S(K) = sum over b of (key(b) <= K ? p_b : 0) taken by a fixed butterfly:
+// S is monotone in K, so K* is found by binary search, first over the mass
+// bits, then over the ids that tie on them. No sort and no barrier.
+
+HSAKV_DEV float masked_sum(const float* p, const unsigned* mb, int NPL_, unsigned M, int I,
+                           bool use_id, int lane) {
+    float acc = 0.f;
+    for (int j = 0; j < NPL_; ++j) {
+        const int b = lane + 64 * j;
+        const bool in = mb[j] < M || (mb[j] == M && (!use_id || b <= I));
+        acc += in ? p[j] : 0.f;
+    }
+    return wave_sum(acc);
+}
+
+template <int NPL>
+__global__ void __launch_bounds__(256)
+k_select_wave(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
+              const int32_t* __restrict__ n_sel_p, TauArg tau, int32_t* __restrict__ sel_count,
+              int32_t* __restrict__ sel_idx, uint8_t* __restrict__ sel_mask,
+              float* __restrict__ block_mass) {
+    __shared__ float qrow_s[4][128];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    const bool live = row < g.H * g.NQB;
+    const int h = live ? row / g.NQB : 0;
+    const int i = live ? row % g.NQB : 0;
+    const int n_sel = *n_sel_p;
+    const int NB = hist_blocks(g, n_sel) + g.NBc;
+    float* qrow = qrow_s[wave];
+    for (int e = lane; e < g.d; e += 64) qrow[e] = live ? qb[((size_t)h * g.NQB + i) * g.d + e] : 0.f;
+    __syncthreads();
+    if (!live) return;
+
+    // pooled logits, one block per lane and item
+    const float inv_sqrt_d = 1.0f / sqrtf((float)g.d);
+    const float* kbh = kb + (size_t)h * g.NB_max * g.d;
+    float p[NPL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int b = lane + 64 * j;
+        float z = -INFINITY;
+        if (b < NB) {
+            const float4* kr = reinterpret_cast<const float4*>(kbh + (size_t)b * g.d);
+            const float4* qr = reinterpret_cast<const float4*>(qrow);
+            float s = 0.f;
+            for (int e = 0; e < g.d / 4; ++e) {
+                const float4 kv = kr[e], qv = qr[e];
+                s = fmaf(qv.x, kv.x, s);
+                s = fmaf(qv.y, kv.y, s);
+                s = fmaf(qv.z, kv.z, s);
+                s = fmaf(qv.w, kv.w, s);
+            }
+            z = s * inv_sqrt_d;
+        }
+        p[j] = z;
+        mx = fmaxf(mx, z);
+    }
+    mx = wave_max(mx);
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const float e = lane + 64 * j < NB ? expf(p[j] - mx) : 0.f;
+        p[j] = e;
+        part += e;
+    }
+    const float inv_total = 1.0f / wave_sum(part);
+    unsigned mb[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const bool ok = lane + 64 * j < NB;
+        p[j] = ok ? p[j] * inv_total : 0.f;
+        mb[j] = ok ? ~__float_as_uint(p[j]) : 0xffffffffu;    // padding sorts last
+    }
+    if (block_mass) {
+        float* dst = block_mass + ((size_t)h * g.NQB + i) * g.NB_max;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+            if (lane + 64 * j < NB) dst[lane + 64 * j] = p[j];
+    }
+
+    // threshold key (M*, I*)
+    const float t = tau.v[h];
+    unsigned Mst = 0xffffffffu;
+    int Ist = NB - 1;
+    bool all = t >= 1.0f;
+    if (!all) {
+        if (masked_sum(p, mb, NPL, 0xffffffffu, 0, false, lane) < t) {
+            all = true;                                  // rounding kept the total below tau
+        } else {
+            unsigned lo = 0, hi = 0xffffffffu;           // smallest M with S(M, all ids) >= t
+            while (lo < hi) {
+                const unsigned mid = lo + ((hi - lo) >> 1);
+                if (masked_sum(p, mb, NPL, mid, 0, false, lane) >= t) hi = mid; else lo = mid + 1;
+            }
+            Mst = lo;
+            int ilo = 0, ihi = NB - 1;                    // smallest id among the ties
+            while (ilo < ihi) {
+                const int mid = (ilo + ihi) >> 1;
+                if (masked_sum(p, mb, NPL, Mst, mid, true, lane) >= t) ihi = mid; else ilo = mid + 1;
+            }
+            Ist = ilo;
+        }
+    }
+
+    // ascending compaction of {b : key(b) <= (M*, I*)}
+    int32_t* out = sel_idx + ((size_t)h * g.NQB + i) * g.NB_max;
+    uint8_t* mk = sel_mask ? sel_mask + ((size_t)h * g.NQB + i) * g.NB_max : nullptr;
+    int pos = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int b = lane + 64 * j;
+        const bool f = b < NB && (all || mb[j] < Mst || (mb[j] == Mst && b <= Ist));
+        const unsigned long long bal = __ballot(f);
+        if (f) out[pos + __popcll(bal & ((1ull << lane) - 1ull))] = b;
+        if (mk && b < NB) mk[b] = (uint8_t)f;
+        pos += __popcll(bal);
+    }
+    if (lane == 0) sel_count[(size_t)h * g.NQB + i] = pos;
+}
+
 void launch_select(const Geo& g, const float* qb, const float* kb, const int32_t* n_sel,
                    const TauArg& tau_dev, int32_t* sel_count, int32_t* sel_idx, uint8_t* sel_mask,
                    float* block_mass, hipStream_t st) {
-    hipLaunchKernelGGL(k_select, dim3(g.H * g.NQB), dim3(kSelThreads), 0, st, g, qb, kb, n_sel,
+    const int rows = g.H * g.NQB;
+    const int per_lane = (g.NB_max + 63) / 64;
+    if (g.d <= 128 && per_lane <= 32) {
+        const dim3 grid((rows + 3) / 4);
+#define HSAKV_SEL(NPL)                                                                            \
+    hipLaunchKernelGGL(k_select_wave<NPL>, grid, dim3(256), 0, st, g, qb, kb, n_sel, tau_dev,      \
+                       sel_count, sel_idx, sel_mask, block_mass)
+        if (per_lane <= 2) HSAKV_SEL(2);
+        else if (per_lane <= 8) HSAKV_SEL(8);
+        else if (per_lane <= 16) HSAKV_SEL(16);
+        else HSAKV_SEL(32);
+#undef HSAKV_SEL
+        return;
+    }
+    hipLaunchKernelGGL(k_select, dim3(rows), dim3(kSelThreads), 0, st, g, qb, kb, n_sel,
                        tau_dev, sel_count, sel_idx, sel_mask, block_mass);
 }

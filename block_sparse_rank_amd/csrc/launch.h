@@ -47,6 +47,11 @@ void launch_lowrank_attn(const Geo&, const void* q, const void* k_hi, const void
                          const void* v_lo, const Epi& ep, hipStream_t);
 
 int lowrank_splits(const Geo&);
+bool proj32_eligible(const Geo&);
+int proj32_splits(const Geo&);
+void launch_lowrank_proj32(const Geo&, const void* E, const void* F, const void* k_hist, const void* v_hist,
+                           const void* k_intra, const void* v_intra, const int32_t* n_sel, float* part,
+                           hipStream_t);
 template <typename T>
 void launch_lowrank_proj(const Geo&, const void* E, const void* F, const void* k_hist, const void* v_hist,
                          const void* k_intra, const void* v_intra, const int32_t* n_sel, float* part,

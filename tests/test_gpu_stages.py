@@ -33,6 +33,12 @@ VARIANTS = [
     ("bf16-d128-r64", _variant("tiny", dtype="bf16", d=128, H=3, r=64, Kp=3, P=8,
                                clustered=True, tau_law="uniform", seed=16), {}),
     ("kp4-binter256", _variant("tiny", Kp=4, P=8, Binter=256, Lq=130, seed=17), {}),
+    ("bf16-one-page", _variant("tiny", dtype="bf16", P=3, clustered=True, tau_law="uniform",
+                               seed=18), dict(page_prompt=[1, 0, 1])),
+    ("bf16-odd-Lq77", _variant("tiny", dtype="bf16", Lq=77, tokens_per_frame=25, Psize=4,
+                               clustered=True, tau_law="uniform", seed=19), {}),
+    ("bf16-no-page", _variant("tiny", dtype="bf16", H=4, d=128, clustered=True,
+                              tau_law="uniform", seed=20), dict(cur_prompt=9)),
 ]
 
 
