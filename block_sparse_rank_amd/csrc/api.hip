@@ -90,7 +90,7 @@ size_t ws_select(const Geo& g) {
     return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4);
 }
 
-size_t ws_sparse(const Geo& g) { return align_up((size_t)g.H * g.NQB * 4); }
+size_t ws_sparse(const Geo& g) { return g.elt == 2 ? align_up(sparse_bf16_ws_bytes(g)) : kAlign; }
 
 size_t ws_linear(const Geo& g, int eb) {
     const size_t n = (size_t)g.r * g.HD;
@@ -306,10 +306,10 @@ HSAKV_API int hsa_sparse_attn(const hsakv_dims* dims, const void* q, const void*
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
         launch_sparse_attn<bf16_t>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
-                                   sel_idx, nullptr, ep, st);
+                                   sel_idx, ws, ep, st);
     else
         launch_sparse_attn<float>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
-                                  sel_idx, nullptr, ep, st);
+                                  sel_idx, ws, ep, st);
     return done();
 }
 
@@ -382,7 +382,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     float* partial = (float*)c.take(ws_gather(g));
     float* qb = (float*)c.take((size_t)g.H * g.NQB * g.d * 4);
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
-    (void)c.take(ws_sparse(g));
+    void* sparse_ws = c.take(ws_sparse(g));
     int32_t* page_idx = (int32_t*)c.take((size_t)g.Kp * 4);
     int32_t* n_sel = (int32_t*)c.take(4);
     void* k_hist = c.take((size_t)g.hist_rows * g.HD * eb);
@@ -408,7 +408,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         run_linear<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
                            in->F, o_linear, nullptr, nullptr, c, st);
         launch_sparse_attn<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,
-                                   sel_count, sel_idx, nullptr, ep, st);
+                                   sel_count, sel_idx, sparse_ws, ep, st);
     } else {
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
@@ -417,7 +417,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         run_linear<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
                           in->F, o_linear, nullptr, nullptr, c, st);
         launch_sparse_attn<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,
-                                  sel_count, sel_idx, nullptr, ep, st);
+                                  sel_count, sel_idx, sparse_ws, ep, st);
     }
     return c.ok ? done() : HSAKV_ERR_WORKSPACE;
 }

@@ -401,13 +401,14 @@ template <typename T>
 void launch_sparse_attn(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
                         const void* k_intra, const void* v_intra, const int32_t* n_sel,
                         const int32_t* sel_count, const int32_t* sel_idx,
-                        const int32_t* row_order, const Epi& ep, hipStream_t st) {
+                        void* ws, const Epi& ep, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        // bf16: the 32x32x16 MFMA kernel with transpose reads (k_sparse32.hip)
+        // bf16: the balanced 32x32x16 MFMA kernels (k_sparse32.hip)
         launch_sparse_attn_bf16_mfma32(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
-                                       sel_idx, ep, st);
+                                       sel_idx, ws, ep, st);
         return;
     }
+    const int32_t* row_order = nullptr;
     dim3 grid(g.H * g.NQB);
     if (g.d == 128)
         hipLaunchKernelGGL((k_sparse_attn<T, 128>), grid, dim3(kAttnThreads), 0, st, g, (const T*)q,
@@ -420,10 +421,10 @@ void launch_sparse_attn(const Geo& g, const void* q, const void* k_hist, const v
 }
 template void launch_sparse_attn<float>(const Geo&, const void*, const void*, const void*,
                                         const void*, const void*, const int32_t*, const int32_t*,
-                                        const int32_t*, const int32_t*, const Epi&, hipStream_t);
+                                        const int32_t*, void*, const Epi&, hipStream_t);
 template void launch_sparse_attn<bf16_t>(const Geo&, const void*, const void*, const void*,
                                          const void*, const void*, const int32_t*, const int32_t*,
-                                         const int32_t*, const int32_t*, const Epi&, hipStream_t);
+                                         const int32_t*, void*, const Epi&, hipStream_t);
 
 template <typename T>
 void launch_lowrank_attn(const Geo& g, const void* q, const void* k_hi, const void* v_hi,

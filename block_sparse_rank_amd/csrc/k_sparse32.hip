@@ -5,10 +5,19 @@
 // selected key blocks only (Binter-token history blocks, Bintra-token chunk
 // blocks).
 //
-// Work-group = 4 waves = two rows (query blocks 2p and 2p+1 of one head,
-// 64 queries each); each wave owns 32 queries. The work-group walks the
-// union of the two rows' selected blocks in ascending order, 64 keys per
-// tile; a tile is loaded once and each wave computes it only if its own row
+// Work decomposition. Query blocks (rows) are taken four at a time: a group
+// is rows 4j..4j+3 of one head, and its work is the union of the four rows'
+// selected blocks, cut into 64-key tiles. A plan kernel writes each group's
+// union in ascending block order with the tile offset of every entry, and the
+// group tile totals are scanned into one global tile sequence. The attention
+// kernel then gives work-group k the tiles [kT/G, (k+1)T/G) of that sequence
+// (T tiles, G work-groups, one per CU), so every CU gets the same number of
+// tiles whatever the rows' selection sizes. A group whose tiles are split
+// between work-groups leaves per-segment softmax partials (running max, row
+// sum, unnormalised output) that a combine kernel merges in a fixed order.
+//
+// Work-group = 8 waves = the 4 rows of the current group, 32 queries per wave.
+// A tile is loaded once into LDS and each wave computes it only if its own row
 // selected it. K and V tiles stay row-major in LDS:
 //   S^T = K Q^T        A = K rows (ds_read_b128), B = Q^T held in registers
 //   O^T += V^T P^T     A = V^T via ds_read_b64_tr_b16 transpose reads,
@@ -22,23 +31,27 @@
 // d0 + i of the four rows K0..K0+3 when lane j of the group addresses row
 // K0 + j/4, columns d0 + 4(j%4)..+3.
 //
-// Tiles arrive by global -> LDS DMA into two LDS buffers: the next tile's
-// DMA is issued before the current tile is computed, so HBM/L2 latency
-// overlaps the MFMA work and no registers hold the data in flight. Work-groups
-// are mapped XCD-aware: work-group b runs on XCD b % 8 and takes row pair
-// (b % 8) * pairs_per_xcd + b / 8, so the rows of one head stay on one XCD
-// and share its L2.
+// Tiles arrive by global -> LDS DMA into a ring of four LDS buffers, sent
+// three tiles ahead of the one being computed, so the L2/HBM latency of a
+// tile is covered by three tiles of MFMA work and no registers hold data in
+// flight. Work-group b runs on XCD b % 8 and takes range (b % 8) * G/8 + b / 8,
+// so neighbouring ranges (neighbouring rows of one head, which select mostly
+// the same blocks) share an XCD's L2.
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
-constexpr int KT = 64;               // keys per tile
+constexpr int KT = 64;            // keys per tile
+constexpr int R = 4;              // rows (query blocks) per group
+constexpr int NW = 2 * R;         // waves per work-group, 32 queries each
+constexpr int kPlanThreads = 256;
+constexpr int kSparseMaxWg = 256; // attention work-groups at most (partials are sized for it)
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;   // native 16-byte vector
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // LDS tiles are filled by global_load_lds_dwordx4 (global -> LDS DMA, no
 // registers): one wave instruction writes 64 lanes x 16 bytes contiguously,
@@ -48,32 +61,29 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;   // native 16
 //   V: slot s of row r holds chunk s ^ (2r mod CPR)       (4 rows, two chunks)
 template <int D>
 struct Lay {
-    static constexpr int ROWB = D * 2;        // bytes per key row
-    static constexpr int CPR = D / 8;         // 16-byte chunks per row
-    static constexpr int MAT = KT * ROWB;     // bytes of one K or V tile
-    static constexpr int BUF = 2 * MAT;       // K tile then V tile
+    static constexpr int ROWB = D * 2;                    // bytes per key row
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int MAT = KT * ROWB;                 // bytes of one K or V tile
+    static constexpr int BUF = 2 * MAT;                   // K tile then V tile
+    static constexpr int INSTR = KT * CPR / 64;           // wave instructions per matrix
+    static constexpr int PER_WAVE = INSTR / NW;           // per wave and matrix
+    static constexpr int VM_PER_TILE = 2 * PER_WAVE;      // vector-memory ops per wave and tile
+    static_assert(INSTR % NW == 0, "DMA instructions split evenly over the waves");
     HSAKV_DEV static int swz_k(int r) { return r & (CPR - 1); }
     HSAKV_DEV static int swz_v(int r) { return (2 * r) & (CPR - 1); }
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// DMA one tile (64 key rows of K and V) into an LDS buffer. Each of the NW
-// waves issues its share of the 1 KB wave instructions. Rows past `nvalid`
+// DMA one tile (64 key rows of K and V) into an LDS buffer. Rows past `nvalid`
 // (the ragged end of a block) load the last valid row: their scores are
 // masked to -inf, so P = 0 multiplies finite values.
-template <int D, int NW>
-HSAKV_DEV void dma_tile(char* buf, const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs,
-                        long long t0, int nvalid, int HD) {
+template <int D>
+HSAKV_DEV void dma_tile(char* buf, const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb,
+                        int nvalid, int HD) {
     using LY = Lay<D>;
-    constexpr int INSTR = KT * LY::CPR / 64;       // wave instructions per matrix
-    constexpr int PER_WAVE = INSTR / NW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const bf16_t* kb = ks + t0 * (long long)HD;
-    const bf16_t* vb = vs + t0 * (long long)HD;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-        const int slot0 = (wave * PER_WAVE + j) * 64;
+    for (int j = 0; j < LY::PER_WAVE; ++j) {
+        const int slot0 = (wave * LY::PER_WAVE + j) * 64;
         const int L = slot0 + lane;
         const int r = L / LY::CPR, sl = L % LY::CPR;
         const int rg = r < nvalid ? r : nvalid - 1;
@@ -84,8 +94,19 @@ HSAKV_DEV void dma_tile(char* buf, const bf16_t* __restrict__ ks, const bf16_t* 
     }
 }
 
-// s_waitcnt vmcnt(0) with the other counters unconstrained (gfx9 encoding).
-HSAKV_DEV void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt vmcnt(N) with the other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+HSAKV_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// Work-group barrier that orders LDS only: this wave's LDS accesses are
+// complete, while its global loads and LDS DMA still in flight stay in flight
+// (a full __syncthreads would wait for them). The memory clobber keeps the
+// compiler from moving memory accesses across it.
+HSAKV_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D>
 struct Wave {
@@ -93,7 +114,7 @@ struct Wave {
     static constexpr int DT = D / 32;   // 32-row tiles of O^T
     bf16x8_t qf[KS];
     f32x16_t o[DT];
-    float m, l;
+    float m, l;                         // running max (log2 units), this lane's share of the row sum
 };
 
 template <int D>
@@ -177,15 +198,13 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
 
 // Key block b -> token range and source (history blocks first, then chunk blocks).
 struct Cursor {
-    int n;          // position in the row's selected-block list
-    int s0;         // offset of the tile inside the block
     long long t0;   // first token of the block
     int len;        // valid tokens of the block
     bool hist;
 };
 
-HSAKV_DEV void open_block(const Geo& g, int NBh, long long Lh, int b, Cursor& c) {
-    c.s0 = 0;
+HSAKV_DEV Cursor open_block(const Geo& g, int NBh, long long Lh, int b) {
+    Cursor c;
     if (b < NBh) {
         c.hist = true;
         c.t0 = (long long)b * g.Binter;
@@ -197,137 +216,162 @@ HSAKV_DEV void open_block(const Geo& g, int NBh, long long Lh, int b, Cursor& c)
         const long long e = c.t0 + g.Bintra < g.Lq ? c.t0 + g.Bintra : g.Lq;
         c.len = (int)(e - c.t0);
     }
+    return c;
 }
 
-// The union of R rows' sorted block lists, walked tile by tile. All threads
-// of the work-group hold the same cursor.
-template <int R>
-struct Union {
-    int pos[R];     // next unread position in each row's list
-    int head[R];    // id at pos (INT_MAX when the list is exhausted)
-    int blk;        // current block
-    unsigned in;    // rows that selected the current block
-};
+HSAKV_DEV int groups_per_head(const Geo& g) { return (g.NQB + R - 1) / R; }
 
-template <int R>
-HSAKV_DEV void union_next(Union<R>& u, const int32_t* const ids[R], const int cnt[R]) {
-    int b = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < R; ++r) b = u.head[r] < b ? u.head[r] : b;
-    u.blk = b;
-    u.in = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (u.head[r] == b && b != 0x7fffffff) {
-            u.in |= 1u << r;
-            ++u.pos[r];
-            u.head[r] = u.pos[r] < cnt[r] ? ids[r][u.pos[r]] : 0x7fffffff;
-        }
+// Largest index i in [0, n) with a[i] <= x, for nondecreasing a with
+// a[0] <= x: a 64-way search by one wave (uniform result).
+HSAKV_DEV int last_le(const int32_t* __restrict__ a, int n, int x) {
+    const int lane = threadIdx.x & 63;
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        const int step = (hi - lo + 63) / 64;
+        const int idx = lo + lane * step;
+        const bool ok = idx < hi && a[idx] <= x;
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(ok);
+        const int jl = 63 - __builtin_clzll(m);   // lane 0 always qualifies
+        lo += jl * step;
+        hi = lo + step < hi ? lo + step : hi;
     }
+    return lo;
 }
 
-// R rows (query blocks 2p, 2p+1, ... of one head) per work-group, 2 waves per
-// row. The work-group stages the union of the rows' selected tiles once;
-// each wave computes only the tiles its own row selected.
-template <int D, int R>
-__global__ void __launch_bounds__(128 * R, 2)
-k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_hist,
-                const bf16_t* __restrict__ v_hist, const bf16_t* __restrict__ k_intra,
-                const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
-                const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx,
-                int groups_per_xcd, Epi ep) {
-    constexpr int NW = 2 * R;
-    // two distinct LDS objects with fixed roles per step: the compiler can then
-    // tell the next tile's DMA from this tile's reads and inserts no wait
-    __shared__ __attribute__((aligned(16))) char buf0[Lay<D>::BUF];
-    __shared__ __attribute__((aligned(16))) char buf1[Lay<D>::BUF];
-    const int b = blockIdx.x;
-    const int grp = (b & 7) * groups_per_xcd + (b >> 3);
-    const int gph = (g.NQB + R - 1) / R;            // groups per head
-    if (grp >= g.H * gph) return;
-    const int h = grp / gph;
-    const int i0 = (grp % gph) * R;                  // first query block of the group
+// Exclusive scan of one int per thread over a work-group of NT threads;
+// *tot receives the sum over the work-group.
+template <int NT>
+HSAKV_DEV int block_excl_scan(int v, int* tot, int* wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int myr = wave >> 1;                       // this wave's row in the group
-    const int g2 = lane >> 5;
-    const int i = i0 + myr;
-    const int query = i * g.Bq + 32 * (wave & 1) + (lane & 31);
+    int s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(s, o, 64);
+        if (lane >= o) s += t;
+    }
+    if (lane == 63) wsum[wave] = s;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int x = wsum[w];
+        before += w < wave ? x : 0;
+        all += x;
+    }
+    __syncthreads();
+    *tot = all;
+    return before + s - v;
+}
+
+// ---- plan ------------------------------------------------------------------
+
+// Union of the selected blocks of one group's rows, in ascending block order:
+// uni[e] = block | row_mask << 16 and upre[e] = tiles of the entries before e.
+__global__ void __launch_bounds__(kPlanThreads)
+k_plan_groups(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
+              const int32_t* __restrict__ sel_idx, int32_t* __restrict__ uni, int32_t* __restrict__ upre,
+              int32_t* __restrict__ gcount, int32_t* __restrict__ gtiles) {
+    __shared__ int mask[4096];
+    __shared__ int wsum[2][kPlanThreads / 64];
+    const int grp = blockIdx.x, tid = threadIdx.x;
+    const int gph = groups_per_head(g);
+    const int h = grp / gph, i0 = (grp % gph) * R;
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
+    const int NB = NBh + g.NBc;
     const long long Lh = (long long)n_sel * g.Tp;
-    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-    const long long hoff = (long long)h * D;
-
-    Wave<D> w;
+    for (int b = tid; b < NB; b += kPlanThreads) mask[b] = 0;
+    __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < Wave<D>::KS; ++ks) {
-        if (i < g.NQB && query < g.Lq)
-            w.qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + (long long)query * g.HD + hoff + 16 * ks + 8 * g2);
-        else
-            w.qf[ks] = bf16x8_t{};
+    for (int r = 0; r < R; ++r) {
+        const int i = i0 + r;
+        if (i >= g.NQB) break;
+        const int row = h * g.NQB + i;
+        const int c = sel_count[row];
+        const int32_t* ids = sel_idx + (size_t)row * g.NB_max;
+        for (int j = tid; j < c; j += kPlanThreads) {
+            const int b = ids[j];
+            if (b >= 0 && b < NB) atomicOr(&mask[b], 1 << r);
+        }
     }
+    __syncthreads();
+    const int per = (NB + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = tid * per, b1 = b0 + per < NB ? b0 + per : NB;
+    int ne = 0, nt = 0;
+    for (int b = b0; b < b1; ++b)
+        if (mask[b]) {
+            ++ne;
+            nt += (open_block(g, NBh, Lh, b).len + KT - 1) / KT;
+        }
+    int ce_tot, ct_tot;
+    int ce = block_excl_scan<kPlanThreads>(ne, &ce_tot, wsum[0]);
+    int ct = block_excl_scan<kPlanThreads>(nt, &ct_tot, wsum[1]);
+    int32_t* u = uni + (size_t)grp * g.NB_max;
+    int32_t* p = upre + (size_t)grp * g.NB_max;
+    for (int b = b0; b < b1; ++b) {
+        const int mk = mask[b];
+        if (mk) {
+            u[ce] = b | (mk << 16);
+            p[ce] = ct;
+            ++ce;
+            ct += (open_block(g, NBh, Lh, b).len + KT - 1) / KT;
+        }
+    }
+    if (tid == 0) {
+        gcount[grp] = ce_tot;
+        gtiles[grp] = ct_tot;
+    }
+}
+
+// gstart[p] = tiles of the groups before p; gstart[NG] = all tiles.
+__global__ void __launch_bounds__(1024) k_plan_scan(int NG, const int32_t* __restrict__ gtiles,
+                                                    int32_t* __restrict__ gstart) {
+    __shared__ int wsum[16];
+    int carry = 0;
+    for (int base = 0; base < NG; base += 1024) {
+        const int p = base + threadIdx.x;
+        const int v = p < NG ? gtiles[p] : 0;
+        int tot;
+        const int ex = block_excl_scan<1024>(v, &tot, wsum);
+        if (p < NG) gstart[p] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) gstart[NG] = carry;
+}
+
+// ---- attention ---------------------------------------------------------------
+
+struct PlanArgs {
+    float* part_o;     // [G][2][NW][DT][64 lanes][16]: unnormalised O of split groups
+    float2* part_ml;   // [G][2][NW][64 lanes]: (running max, lane's row-sum share)
+    int NG, G;
+};
+
+HSAKV_DEV int range_start(long long k, int T, int G) { return (int)(k * T / G); }
+
+// Loads the 32 queries of this wave (zeros past the chunk) and clears the state.
+template <int D>
+HSAKV_DEV void start_rows(const Geo& g, const bf16_t* __restrict__ q, int h, int i, Wave<D>& w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int query = i * g.Bq + 32 * (wave & 1) + (lane & 31);
+    const bool ok = i < g.NQB && query < g.Lq;
+    const bf16_t* qp = q + (long long)(ok ? query : 0) * g.HD + (long long)h * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < Wave<D>::KS; ++ks)
+        w.qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
 #pragma unroll
     for (int dt = 0; dt < Wave<D>::DT; ++dt) w.o[dt] = f32x16_t{};
     w.m = -INFINITY;
     w.l = 0.f;
+}
 
-    const int32_t* ids[R];
-    int cnt[R];
-    Union<R> u;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int ir = i0 + r;
-        const int row = h * g.NQB + ir;
-        cnt[r] = ir < g.NQB ? sel_count[row] : 0;
-        ids[r] = sel_idx + (size_t)row * g.NB_max;
-        u.pos[r] = 0;
-        u.head[r] = cnt[r] > 0 ? ids[r][0] : 0x7fffffff;
-    }
-    union_next<R>(u, ids, cnt);
-
-    Cursor cur;
-    int nvalid = 0;
-    unsigned in_next = u.in;
-    bool have = u.blk != 0x7fffffff;
-    if (have) {
-        open_block(g, NBh, Lh, u.blk, cur);
-        nvalid = cur.len < KT ? cur.len : KT;
-        dma_tile<D, NW>(buf0, (cur.hist ? k_hist : k_intra) + hoff, (cur.hist ? v_hist : v_intra) + hoff,
-                        cur.t0, nvalid, g.HD);
-    }
-    // One pipeline step: the current tile sits in `now`, the next one is sent to `nxt`.
-    auto step = [&](const char* now, char* nxt) __attribute__((always_inline)) {
-        // this wave's DMA of the current tile has landed; the barrier makes every
-        // wave's part visible and retires every read of `nxt` by the last step
-        wait_vmcnt0();
-        __syncthreads();
-        const int nvalid_now = nvalid;
-        const unsigned in_now = in_next;
-        cur.s0 += KT;
-        if (cur.s0 >= cur.len) {
-            union_next<R>(u, ids, cnt);
-            have = u.blk != 0x7fffffff;
-            if (have) {
-                open_block(g, NBh, Lh, u.blk, cur);
-                in_next = u.in;
-            }
-        }
-        if (have) {
-            nvalid = cur.len - cur.s0 < KT ? cur.len - cur.s0 : KT;
-            dma_tile<D, NW>(nxt, (cur.hist ? k_hist : k_intra) + hoff, (cur.hist ? v_hist : v_intra) + hoff,
-                            cur.t0 + cur.s0, nvalid, g.HD);
-        }
-        if ((in_now >> myr) & 1u) tile_step<D>(w, now, now + Lay<D>::MAT, nvalid_now, scale_log2);
-    };
-    while (have) {
-        step(buf0, buf1);
-        if (!have) break;
-        step(buf1, buf0);
-    }
-    if (i >= g.NQB) return;
-
-    // epilogue: O / l, optional gated fusion with the low-rank branch
-    float lt = w.l + __shfl_xor(w.l, 32, 64);
+// O / l and the optional gated fusion with the low-rank branch.
+template <int D>
+HSAKV_DEV void finish_rows(const Geo& g, const Epi& ep, int h, int i, const Wave<D>& w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g2 = lane >> 5;
+    const int query = i * g.Bq + 32 * (wave & 1) + (lane & 31);
+    const float lt = w.l + __shfl_xor(w.l, 32, 64);
     const float inv_l = lt > 0.f ? 1.0f / lt : 0.f;
     float gate = 0.f;
     if (ep.out) {
@@ -342,8 +386,8 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         const float z = expf(-fabsf(x));
         gate = x >= 0.f ? 1.0f / (1.0f + z) : z / (1.0f + z);
     }
-    if (query >= g.Lq) return;
-    const long long base = (long long)query * g.HD + hoff;
+    if (i >= g.NQB || query >= g.Lq) return;
+    const long long base = (long long)query * g.HD + (long long)h * D;
     if (ep.gate && g2 == 0) ep.gate[(long long)query * g.H + h] = gate;
 #pragma unroll
     for (int dt = 0; dt < Wave<D>::DT; ++dt) {
@@ -368,28 +412,272 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     }
 }
 
+template <int D>
+HSAKV_DEV size_t part_index(int slot, int wave, int dt, int lane) {
+    return ((((size_t)slot * NW + wave) * Wave<D>::DT + dt) * 64 + lane) * 16;
+}
+
+// Work-group k computes tiles [kT/G, (k+1)T/G) of the global tile sequence.
+template <int D>
+__global__ void __launch_bounds__(64 * NW)
+k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_hist,
+                const bf16_t* __restrict__ v_hist, const bf16_t* __restrict__ k_intra,
+                const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
+                const int32_t* __restrict__ uni, const int32_t* __restrict__ upre,
+                const int32_t* __restrict__ gcount, const int32_t* __restrict__ gtiles,
+                const int32_t* __restrict__ gstart, PlanArgs pl, int per_xcd, Epi ep) {
+    using LY = Lay<D>;
+    // four distinct LDS objects with fixed roles per unrolled step: the
+    // compiler can tell the tiles' DMA from the reads and inserts no wait
+    __shared__ __attribute__((aligned(16))) char lds0[LY::BUF];
+    __shared__ __attribute__((aligned(16))) char lds1[LY::BUF];
+    __shared__ __attribute__((aligned(16))) char lds2[LY::BUF];
+    __shared__ __attribute__((aligned(16))) char lds3[LY::BUF];
+    const int b = blockIdx.x;
+    const int k = (b & 7) * per_xcd + (b >> 3);
+    if (k >= pl.G) return;
+    const int T = gstart[pl.NG];
+    const int a0 = range_start(k, T, pl.G), a1 = range_start(k + 1, T, pl.G);
+    const int total = a1 - a0;
+    if (total <= 0) return;
+
+    const int wave = threadIdx.x >> 6;
+    const int myr = wave >> 1;
+    const int n_sel = *n_sel_p;
+    const int NBh = hist_blocks(g, n_sel);
+    const long long Lh = (long long)n_sel * g.Tp;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    const int gph = groups_per_head(g);
+
+    // producer position: the next tile to send
+    int pg = last_le(gstart, pl.NG, a0);
+    const int first_grp = pg;
+    int pcnt = gcount[pg];
+    int pe = last_le(upre + (size_t)pg * g.NB_max, pcnt, a0 - gstart[pg]);
+    int pt = a0 - gstart[pg] - upre[(size_t)pg * g.NB_max + pe];
+    int pmask, pntile;
+    Cursor pc;
+    auto load_entry = [&]() __attribute__((always_inline)) {
+        const int v = uni[(size_t)pg * g.NB_max + pe];
+        pmask = v >> 16;
+        pc = open_block(g, NBh, Lh, v & 0xffff);
+        pntile = (pc.len + KT - 1) / KT;
+    };
+    load_entry();
+    // next tile of the same group (the caller knows one exists)
+    auto advance = [&]() __attribute__((always_inline)) {
+        if (++pt >= pntile) {
+            pt = 0;
+            ++pe;
+            load_entry();
+        }
+    };
+
+    Wave<D> w;
+    int n = 0;        // tiles of the range computed
+    int issued = 0;   // tiles of the range sent
+    while (true) {
+        // one group per pass: its tiles [n, end) of this range, with the ring
+        // refilled from the first buffer (a pipeline drain per group change)
+        const int grp = pg;
+        const int h = grp / gph, i = (grp % gph) * R + myr;
+        const int S = gstart[grp], Tg = gtiles[grp];
+        const int end = (S + Tg < a1 ? S + Tg : a1) - a0;
+        const long long hoff = (long long)h * D;
+        start_rows<D>(g, q, h, i, w);
+        // tile info for the consumer: row mask << 7 | valid keys
+        int info0 = 0, info1 = 0, info2 = 0, info3 = 0;
+        auto issue = [&](char* dst) __attribute__((always_inline)) -> int {
+            const int nvalid = pc.len - pt * KT < KT ? pc.len - pt * KT : KT;
+            const long long t0 = pc.t0 + (long long)pt * KT;
+            const bf16_t* kb = (pc.hist ? k_hist : k_intra) + hoff + t0 * g.HD;
+            const bf16_t* vb = (pc.hist ? v_hist : v_intra) + hoff + t0 * g.HD;
+            dma_tile<D>(dst, kb, vb, nvalid, g.HD);
+            const int inf = (pmask << 7) | nvalid;
+            if (++issued < end) advance();
+            return inf;
+        };
+        info0 = issue(lds0);
+        if (issued < end) info1 = issue(lds1);
+        if (issued < end) info2 = issue(lds2);
+        auto step = [&](const char* now, char* nxt, int inf, int& inf_nxt) __attribute__((always_inline)) {
+            // this wave's DMA of tile n has landed once at most the tiles sent
+            // after it are outstanding; the barrier makes every wave's part
+            // visible and retires every read of `nxt` (tile n - 1)
+            const int later = issued - n - 1;
+            if (later >= 2)
+                wait_vmcnt<2 * LY::VM_PER_TILE>();
+            else if (later == 1)
+                wait_vmcnt<LY::VM_PER_TILE>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier();
+            if (issued < end) inf_nxt = issue(nxt);
+            if ((inf >> (7 + myr)) & 1) tile_step<D>(w, now, now + LY::MAT, inf & 127, scale_log2);
+        };
+        while (true) {
+            step(lds0, lds3, info0, info3);
+            if (++n == end) break;
+            step(lds1, lds0, info1, info0);
+            if (++n == end) break;
+            step(lds2, lds1, info2, info1);
+            if (++n == end) break;
+            step(lds3, lds2, info3, info2);
+            if (++n == end) break;
+        }
+        if (S >= a0 && S + Tg <= a1) {
+            finish_rows<D>(g, ep, h, i, w);
+        } else {
+            const int slot = 2 * k + (grp == first_grp ? 0 : 1);
+            const int lane = threadIdx.x & 63;
+#pragma unroll
+            for (int dt = 0; dt < Wave<D>::DT; ++dt) {
+                float4* po = reinterpret_cast<float4*>(pl.part_o + part_index<D>(slot, wave, dt, lane));
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    po[c] = float4{w.o[dt][4 * c], w.o[dt][4 * c + 1], w.o[dt][4 * c + 2], w.o[dt][4 * c + 3]};
+            }
+            pl.part_ml[((size_t)slot * NW + wave) * 64 + lane] = float2{w.m, w.l};
+        }
+        if (n == total) break;
+        // next group with tiles; every wave is done with the ring before it refills
+        pe = 0;
+        pt = 0;
+        do {
+            ++pg;
+            pcnt = gcount[pg];
+        } while (pcnt == 0);
+        load_entry();
+        lds_barrier();
+    }
+}
+
+// Groups split between work-groups: merge the segment partials in range order,
+// then the same epilogue. Groups without tiles get O = 0.
+template <int D>
+__global__ void __launch_bounds__(64 * NW)
+k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict__ gtiles,
+                 const int32_t* __restrict__ gstart, PlanArgs pl, Epi ep) {
+    const int grp = blockIdx.x;
+    const int T = gstart[pl.NG];
+    const int S = gstart[grp], Tg = gtiles[grp];
+    const int G = pl.G;
+    int k0 = 0;
+    if (Tg > 0) {
+        // the range holding the group's first tile: largest k with start <= S
+        k0 = (int)((long long)S * G / T);
+        while (k0 + 1 < G && range_start(k0 + 1, T, G) <= S) ++k0;
+        while (k0 > 0 && range_start(k0, T, G) > S) --k0;
+        if (range_start(k0 + 1, T, G) >= S + Tg) return;   // one range holds the whole group
+    }
+    const int gph = groups_per_head(g);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int h = grp / gph, i = (grp % gph) * R + (wave >> 1);
+    Wave<D> w;
+    start_rows<D>(g, q, h, i, w);
+    if (Tg > 0) {
+        for (int kk = k0; kk < G; ++kk) {
+            const int s0 = range_start(kk, T, G);
+            if (s0 >= S + Tg) break;
+            if (range_start(kk + 1, T, G) == s0) continue;   // empty range
+            const int slot = 2 * kk + (s0 < S ? 1 : 0);
+            const float2 ml = pl.part_ml[((size_t)slot * NW + wave) * 64 + lane];
+            const float m_new = fmaxf(w.m, ml.x);
+            const float a_old = w.m == -INFINITY ? 0.f : exp2f(w.m - m_new);
+            const float a_seg = ml.x == -INFINITY ? 0.f : exp2f(ml.x - m_new);
+            w.m = m_new;
+            w.l = w.l * a_old + ml.y * a_seg;
+#pragma unroll
+            for (int dt = 0; dt < Wave<D>::DT; ++dt) {
+                const float4* po = reinterpret_cast<const float4*>(pl.part_o + part_index<D>(slot, wave, dt, lane));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float4 v = po[c];
+                    w.o[dt][4 * c] = w.o[dt][4 * c] * a_old + v.x * a_seg;
+                    w.o[dt][4 * c + 1] = w.o[dt][4 * c + 1] * a_old + v.y * a_seg;
+                    w.o[dt][4 * c + 2] = w.o[dt][4 * c + 2] * a_old + v.z * a_seg;
+                    w.o[dt][4 * c + 3] = w.o[dt][4 * c + 3] * a_old + v.w * a_seg;
+                }
+            }
+        }
+    }
+    finish_rows<D>(g, ep, h, i, w);
+}
+
+// Attention work-groups on the current device: one per CU, at most kSparseMaxWg.
+int sparse_wgs() {
+    static int cache[64] = {0};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return kSparseMaxWg;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = kSparseMaxWg;
+    const int G = cus < kSparseMaxWg ? cus : kSparseMaxWg;
+    if (dev >= 0 && dev < 64) cache[dev] = G;
+    return G;
+}
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct SparseWs {
+    int32_t *uni, *upre, *gcount, *gtiles, *gstart;
+    float* part_o;
+    float2* part_ml;
+};
+
+int n_groups(const Geo& g) { return g.H * ((g.NQB + R - 1) / R); }
+size_t part_o_bytes(const Geo& g) { return al256((size_t)kSparseMaxWg * 2 * NW * 64 * 16 * 4 * (g.d / 32)); }
+size_t part_ml_bytes() { return al256((size_t)kSparseMaxWg * 2 * NW * 64 * 8); }
+
+SparseWs carve(const Geo& g, void* ws) {
+    const int NG = n_groups(g);
+    char* p = (char*)ws;
+    SparseWs s;
+    s.uni = (int32_t*)p;     p += al256((size_t)NG * g.NB_max * 4);
+    s.upre = (int32_t*)p;    p += al256((size_t)NG * g.NB_max * 4);
+    s.gcount = (int32_t*)p;  p += al256((size_t)NG * 4);
+    s.gtiles = (int32_t*)p;  p += al256((size_t)NG * 4);
+    s.gstart = (int32_t*)p;  p += al256((size_t)(NG + 1) * 4);
+    s.part_o = (float*)p;    p += part_o_bytes(g);
+    s.part_ml = (float2*)p;
+    return s;
+}
+
 }  // namespace
 
-template <int D, int R>
-static void launch_r(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
+size_t sparse_bf16_ws_bytes(const Geo& g) {
+    const int NG = n_groups(g);
+    return 2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) + al256((size_t)(NG + 1) * 4) +
+           part_o_bytes(g) + part_ml_bytes();
+}
+
+template <int D>
+static void launch_d(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
                      const void* k_intra, const void* v_intra, const int32_t* n_sel,
-                     const int32_t* sel_count, const int32_t* sel_idx, const Epi& ep,
+                     const int32_t* sel_count, const int32_t* sel_idx, void* ws, const Epi& ep,
                      hipStream_t st) {
-    const int groups = g.H * ((g.NQB + R - 1) / R);
-    const int per_xcd = (groups + 7) / 8;
-    hipLaunchKernelGGL((k_sparse_attn32<D, R>), dim3(8 * per_xcd), dim3(128 * R), 0, st, g,
-                       (const bf16_t*)q, (const bf16_t*)k_hist, (const bf16_t*)v_hist,
-                       (const bf16_t*)k_intra, (const bf16_t*)v_intra, n_sel, sel_count, sel_idx,
+    const int NG = n_groups(g);
+    const SparseWs s = carve(g, ws);
+    hipLaunchKernelGGL(k_plan_groups, dim3(NG), dim3(kPlanThreads), 0, st, g, n_sel, sel_count, sel_idx,
+                       s.uni, s.upre, s.gcount, s.gtiles);
+    hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, NG, (const int32_t*)s.gtiles, s.gstart);
+    PlanArgs pl{s.part_o, s.part_ml, NG, sparse_wgs()};
+    const int per_xcd = (pl.G + 7) / 8;
+    hipLaunchKernelGGL((k_sparse_attn32<D>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
+                       (const bf16_t*)k_hist, (const bf16_t*)v_hist, (const bf16_t*)k_intra,
+                       (const bf16_t*)v_intra, n_sel, (const int32_t*)s.uni, (const int32_t*)s.upre,
+                       (const int32_t*)s.gcount, (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl,
                        per_xcd, ep);
+    hipLaunchKernelGGL((k_sparse_combine<D>), dim3(NG), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
+                       (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl, ep);
 }
 
 void launch_sparse_attn_bf16_mfma32(const Geo& g, const void* q, const void* k_hist,
                                     const void* v_hist, const void* k_intra, const void* v_intra,
                                     const int32_t* n_sel, const int32_t* sel_count,
-                                    const int32_t* sel_idx, const Epi& ep, hipStream_t st) {
-    // two query blocks (rows) of one head per work-group
+                                    const int32_t* sel_idx, void* ws, const Epi& ep, hipStream_t st) {
     if (g.d == 128)
-        launch_r<128, 2>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ep, st);
+        launch_d<128>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ws, ep, st);
     else
-        launch_r<64, 2>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ep, st);
+        launch_d<64>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ws, ep, st);
 }

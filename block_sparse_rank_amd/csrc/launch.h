@@ -37,11 +37,13 @@ void launch_select(const Geo&, const float* qb, const float* kb, const int32_t* 
 template <typename T>
 void launch_sparse_attn(const Geo&, const void* q, const void* k_hist, const void* v_hist, const void* k_intra,
                         const void* v_intra, const int32_t* n_sel, const int32_t* sel_count,
-                        const int32_t* sel_idx, const int32_t* row_order, const Epi& ep, hipStream_t);
+                        const int32_t* sel_idx, void* ws, const Epi& ep, hipStream_t);
+// bf16 path: ws holds sparse_bf16_ws_bytes(g) bytes (plan and split partials)
+size_t sparse_bf16_ws_bytes(const Geo&);
 void launch_sparse_attn_bf16_mfma32(const Geo&, const void* q, const void* k_hist, const void* v_hist,
                                     const void* k_intra, const void* v_intra, const int32_t* n_sel,
-                                    const int32_t* sel_count, const int32_t* sel_idx, const Epi& ep,
-                                    hipStream_t);
+                                    const int32_t* sel_count, const int32_t* sel_idx, void* ws,
+                                    const Epi& ep, hipStream_t);
 template <typename T>
 void launch_lowrank_attn(const Geo&, const void* q, const void* k_hi, const void* v_hi, const void* k_lo,
                          const void* v_lo, const Epi& ep, hipStream_t);

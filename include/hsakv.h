@@ -201,7 +201,11 @@ int hsa_select(const hsakv_dims* dims, const void* q, const void* k_hist, const 
  *   o_sparse[t][h] = sum_j softmax_j(<q[t,h], K[j,h]> / sqrt(d)) V[j,h]
  * over the tokens j of the blocks sel_idx[h][i][0..sel_count[h][i]), where
  * K, V are the key sequence [k_hist rows 0..n_sel*Tp) ; k_intra]. No mask.
- * o_sparse is f32 [Lq][H][d] (device). Workspace: HSAKV_ENTRY_SPARSE. */
+ * o_sparse is f32 [Lq][H][d] (device). Workspace: HSAKV_ENTRY_SPARSE; with
+ * bf16 it holds the work plan (union of the selected blocks of every four
+ * query blocks of a head, tile offsets) and the softmax partials of query
+ * blocks whose tiles are split between work-groups. Its contents are scratch:
+ * calls that overlap in time must not share a workspace. */
 int hsa_sparse_attn(const hsakv_dims* dims, const void* q, const void* k_hist, const void* v_hist,
                     const void* k_intra, const void* v_intra, const int32_t* n_sel,
                     const int32_t* sel_count, const int32_t* sel_idx, float* o_sparse,
