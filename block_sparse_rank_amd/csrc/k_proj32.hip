@@ -13,10 +13,12 @@
 // (r x H*d), so it is split along k; each split writes an f32 partial and a
 // separate pass adds the partials in split order.
 //
-// Work-group = 8 waves, tile 256 (m) x 128 (n), k-step 64. Wave w computes
-// rows 64(w%4).. and columns 64(w/4).. with four 32x32 accumulators. Tiles
+// Work-group = 4 waves, tile 128 (m) x 128 (n), k-step 64. Wave w computes
+// rows 64(w%2).. and columns 64(w/2).. with four 32x32 accumulators. Tiles
 // are brought into LDS by global -> LDS DMA (two buffers, the next k-step in
-// flight during the MFMA work). DMA writes 64 lanes x 16 bytes contiguously,
+// flight during the MFMA work); the tile is small enough that two
+// work-groups share a CU, doubling the DMA in flight of this latency-bound
+// stream. DMA writes 64 lanes x 16 bytes contiguously,
 // so the padded row pitch that keeps the operand reads free of bank conflicts
 // is made by "pad lanes": the X tile has 9 slots per row (8 data + 1 pad,
 // 144 B pitch), the Y tile 18 (16 + 2, 288 B pitch); a pad lane loads any
@@ -28,15 +30,15 @@
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64, NT = 512, NWV = 8;
+constexpr int BM = 128, BN = 128, BK = 64, NT = 256, NWV = 4;
 constexpr int A_SLOTS = BK / 8 + 1;           // 9
 constexpr int B_SLOTS = BN / 8 + 2;           // 18
 constexpr int A_ROWB = A_SLOTS * 16;          // 144
 constexpr int B_ROWB = B_SLOTS * 16;          // 288
-constexpr int A_BYTES = BM * A_ROWB;          // 36864
+constexpr int A_BYTES = BM * A_ROWB;          // 18432
 constexpr int B_BYTES = BK * B_ROWB;          // 18432
-constexpr int STAGE = A_BYTES + B_BYTES;      // 55296; two stages: 110592 bytes
-constexpr int A_INSTR = BM * A_SLOTS / 64;    // 36
+constexpr int STAGE = A_BYTES + B_BYTES;      // 36864; two stages: 73728 bytes (two work-groups per CU)
+constexpr int A_INSTR = BM * A_SLOTS / 64;    // 18
 constexpr int B_INSTR = BK * B_SLOTS / 64;    // 18
 static_assert(BM * A_SLOTS % 64 == 0 && BK * B_SLOTS % 64 == 0, "whole wave instructions");
 
@@ -147,7 +149,7 @@ HSAKV_DEV void zero_tail(char* buf, int first) {
 
 HSAKV_DEV void compute_stage(const char* buf, f32x16_t (&acc)[2][2]) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int mw = wave & 3, nw = wave >> 2;
+    const int mw = wave & 1, nw = wave >> 1;
     const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
     const char* A = buf;
     const char* B = buf + A_BYTES;
@@ -173,7 +175,7 @@ HSAKV_DEV void compute_stage(const char* buf, f32x16_t (&acc)[2][2]) {
     }
 }
 
-__global__ void __launch_bounds__(NT, 1)
+__global__ void __launch_bounds__(NT, 2)
 k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__ F,
                  const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
                  const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
@@ -230,7 +232,7 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 
     // D[m = 8(i/4) + 4(l/32) + i%4][n = l%32] of each 32x32 accumulator
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int mw = wave & 3, nw = wave >> 2, g2 = lane >> 5;
+    const int mw = wave & 1, nw = wave >> 1, g2 = lane >> 5;
     float* out = part + (size_t)(split * 2 + z) * g.r * g.HD;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -254,7 +256,7 @@ bool proj32_eligible(const Geo& g) {
 
 int proj32_splits(const Geo& g) {
     const int tiles = 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
-    int s = (256 + tiles - 1) / tiles;
+    int s = (512 + tiles - 1) / tiles;
     return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
