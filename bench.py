@@ -201,29 +201,70 @@ def stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops, ga
     for fn in stages.values():       # warm and produce each stage's inputs once
         fn()
     torch.cuda.synchronize()
-    ms = {}
+    # each rep runs the stages in forward order, with an event between stages,
+    # so every stage meets the caches as it does inside hsa_forward
+    names = list(stages)
     reps = max(3, a.steps)
-    for name, fn in stages.items():
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms[name] = e0.elapsed_time(e1) / reps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        evs[r][0].record(stream)
+        for j, name in enumerate(names):
+            stages[name]()
+            evs[r][j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = {name: sum(evs[r][j].elapsed_time(evs[r][j + 1]) for r in range(reps)) / reps
+          for j, name in enumerate(names)}
     peak = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_F32_TFLOPS
     att_tflops = sparse_flops / (ms["sparse_attn"] * 1e-3) / 1e12
     gather_gbs = gather_bytes / (ms["gather"] * 1e-3) / 1e9
+    traffic = recorded_traffic("hsa_sparse_attn", s.name)
     return {
         "stages_ms": {k: round(v, 4) for k, v in ms.items()},
-        "roofline": {"kernel": "k_sparse_attn", "bound": "mfma", "achieved": round(att_tflops, 2),
+        "roofline": {"kernel": "hsa_sparse_attn (k_plan_groups, k_plan_scan, k_sparse_attn32, "
+                               "k_sparse_combine)",
+                     "bound": "mfma", "achieved": round(att_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(att_tflops / peak, 4),
-                     "traffic": None, "algorithmic_flops": sparse_flops},
+                     "traffic": traffic, "algorithmic_flops": sparse_flops},
         "gather_roofline": {"kernel": "k_gather (+ retrieval)", "bound": "hbm",
                             "achieved": round(gather_gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gather_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": recorded_traffic("hkv_gather", s.name),
                             "algorithmic_bytes": gather_bytes},
     }
+
+
+# Sources whose kernels a recorded HBM-traffic figure covers; a figure is only
+# reported while the hash of these files matches the one recorded with it.
+TRAFFIC_SOURCES = {
+    "hsa_sparse_attn": ["block_sparse_rank_amd/csrc/k_sparse32.hip", "block_sparse_rank_amd/csrc/common.h",
+                        "block_sparse_rank_amd/csrc/launch.h"],
+    "hkv_gather": ["block_sparse_rank_amd/csrc/k_hkv.hip", "block_sparse_rank_amd/csrc/common.h",
+                   "block_sparse_rank_amd/csrc/launch.h"],
+}
+
+
+def source_hash(entry: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES[entry]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(entry: str, workload: str):
+    """HBM bytes per call of `entry` from the committed rocprofv3 counter record
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is no record for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[entry][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(entry):
+        return None
+    return rec.get("bytes_per_call")
 
 
 def cpu_baseline(s, ch, pool_k, pool_v, budget_s):
