@@ -6,8 +6,9 @@
 // blocks).
 //
 // Work decomposition. Query blocks (rows) are taken four at a time: a group
-// is rows 4j..4j+3 of one head, and its work is the union of the four rows'
-// selected blocks, cut into 64-key tiles. A plan kernel writes each group's
+// is four rows of one head, chosen by a plan kernel so that their selections
+// overlap (greedy, see k_plan_rows), and its work is the union of the four
+// rows' selected blocks, cut into 64-key tiles. A plan kernel writes each group's
 // union in ascending block order with the tile offset of every entry, and the
 // group tile totals are scanned into one global tile sequence. The attention
 // kernel then gives work-group k the tiles [kT/G, (k+1)T/G) of that sequence
@@ -35,8 +36,8 @@
 // three tiles ahead of the one being computed, so the L2/HBM latency of a
 // tile is covered by three tiles of MFMA work and no registers hold data in
 // flight. Work-group b runs on XCD b % 8 and takes range (b % 8) * G/8 + b / 8,
-// so neighbouring ranges (neighbouring rows of one head, which select mostly
-// the same blocks) share an XCD's L2.
+// so neighbouring ranges (groups of one head, which select many of the same
+// blocks) share an XCD's L2.
 #include "common.h"
 #include "launch.h"
 
@@ -45,6 +46,7 @@ namespace {
 constexpr int KT = 64;            // keys per tile
 constexpr int R = 4;              // rows (query blocks) per group
 constexpr int NW = 2 * R;         // waves per work-group, 32 queries each
+constexpr float kLazyMax = 8.0f;  // margin (log2 units) before the running max is raised
 constexpr int kPlanThreads = 256;
 constexpr int kSparseMaxWg = 256; // attention work-groups at most (partials are sized for it)
 
@@ -151,9 +153,12 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sub][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(w.m, mx * scale_log2);
-    const bool moved = m_new > w.m;
-    const float alpha = fast_exp2(w.m - m_new);   // 1 when the max did not move
+    // the running max is raised only when a score passes it by more than
+    // kLazyMax, so O is rarely rescaled; weights stay below 2^kLazyMax
+    const float mt = mx * scale_log2;
+    const bool moved = mt > w.m + kLazyMax;
+    const float m_new = moved ? mt : w.m;
+    const float alpha = moved ? fast_exp2(w.m - m_new) : 1.0f;
     w.m = m_new;
     float rs = 0.f;
 #pragma unroll
@@ -165,7 +170,7 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
             rs += p;
         }
     w.l = w.l * alpha + rs;
-    // rescale O only when some row max of the wave moved
+    // rescale O only when some running max of the wave was raised
     if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
         for (int dt = 0; dt < Wave<D>::DT; ++dt) w.o[dt] *= alpha;
@@ -265,17 +270,117 @@ HSAKV_DEV int block_excl_scan(int v, int* tot, int* wsum) {
 
 // ---- plan ------------------------------------------------------------------
 
+// Rows of each head are grouped R at a time so that a group's rows select
+// mostly the same blocks: the union walk then spends few steps on blocks only
+// some rows selected. Greedy, per head: a group starts from the lowest row
+// not yet grouped and takes, R - 1 times, the remaining row whose selection
+// shares the most tiles with the group's union less the tiles it would add.
+// grows[grp * R + r] = row (NQB past the head's rows). Heads with more than
+// kGroupThreads rows or more than 32 kGroupWords blocks keep consecutive
+// rows. The grouping only orders the work: each row's result is the same.
+constexpr int kGroupWords = 16;
+constexpr int kGroupThreads = 256;
+
+// Tiles of the blocks in word w of a selection bitmask (bit b of word w is
+// block 32 w + b; blocks below NBh are history blocks).
+HSAKV_DEV int mask_tiles(uint32_t x, int w, int NBh, int th, int tc) {
+    const int lo = 32 * w;
+    const uint32_t hm = lo + 32 <= NBh ? ~0u : (lo >= NBh ? 0u : (1u << (NBh - lo)) - 1u);
+    return th * __builtin_popcount(x & hm) + tc * __builtin_popcount(x & ~hm);
+}
+
+// Largest key over the work-group (all threads get it).
+HSAKV_DEV unsigned long long block_max(unsigned long long key, unsigned long long* red) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(key, o, 64);
+        key = t > key ? t : key;
+    }
+    if (lane == 0) red[wv] = key;
+    __syncthreads();
+    unsigned long long m = red[0];
+#pragma unroll
+    for (int i = 1; i < kGroupThreads / 64; ++i) m = red[i] > m ? red[i] : m;
+    __syncthreads();
+    return m;
+}
+
+__global__ void __launch_bounds__(kGroupThreads)
+k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
+            const int32_t* __restrict__ sel_idx, int32_t* __restrict__ grows) {
+    __shared__ uint32_t bits_s[kGroupThreads][kGroupWords];
+    __shared__ uint32_t uni_s[kGroupWords];
+    __shared__ unsigned long long red[kGroupThreads / 64];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int gph = groups_per_head(g);
+    const int n_sel = *n_sel_p;
+    const int NBh = hist_blocks(g, n_sel);
+    const int NB = NBh + g.NBc;
+    int32_t* out = grows + (size_t)h * gph * R;
+    if (NB > 32 * kGroupWords || g.NQB > kGroupThreads) {
+        for (int e = tid; e < gph * R; e += kGroupThreads) out[e] = e < g.NQB ? e : g.NQB;
+        return;
+    }
+    const int th = (g.Binter + KT - 1) / KT, tc = (g.Bintra + KT - 1) / KT;
+    for (int e = tid; e < kGroupThreads * kGroupWords; e += kGroupThreads) (&bits_s[0][0])[e] = 0u;
+    __syncthreads();
+    for (int r = 0; r < g.NQB; ++r) {
+        const int c = sel_count[h * g.NQB + r];
+        const int32_t* ids = sel_idx + (size_t)(h * g.NQB + r) * g.NB_max;
+        for (int j = tid; j < c; j += kGroupThreads) {
+            const int b = ids[j];
+            if (b >= 0 && b < NB) atomicOr(&bits_s[r][b >> 5], 1u << (b & 31));
+        }
+    }
+    __syncthreads();
+    // thread tid holds row tid
+    uint32_t bits[kGroupWords];
+    int own = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupWords; ++w) {
+        bits[w] = bits_s[tid][w];
+        own += mask_tiles(bits[w], w, NBh, th, tc);
+    }
+    bool left = tid < g.NQB;
+    const unsigned long long lowrow = 0xffffffffull - (unsigned)tid;
+    for (int j = 0; j < gph; ++j) {
+        for (int r = 0; r < R; ++r) {
+            unsigned long long key = 0;
+            if (left) {
+                int score = 0;   // the group's first row: the lowest remaining
+                if (r > 0) {
+                    int ov = 0;
+#pragma unroll
+                    for (int w = 0; w < kGroupWords; ++w) ov += mask_tiles(bits[w] & uni_s[w], w, NBh, th, tc);
+                    score = 2 * ov - own;   // shared tiles less the tiles it adds
+                }
+                key = ((unsigned long long)(unsigned)(score + (1 << 20)) << 32) | lowrow;
+            }
+            const unsigned long long m = block_max(key, red);
+            const int pick = m ? (int)(0xffffffffu - (unsigned)(m & 0xffffffffull)) : g.NQB;
+            if (tid == 0) out[j * R + r] = pick;
+            if (m && pick == tid) {
+                left = false;
+#pragma unroll
+                for (int w = 0; w < kGroupWords; ++w) uni_s[w] = r == 0 ? bits[w] : (uni_s[w] | bits[w]);
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // Union of the selected blocks of one group's rows, in ascending block order:
 // uni[e] = block | row_mask << 16 and upre[e] = tiles of the entries before e.
 __global__ void __launch_bounds__(kPlanThreads)
 k_plan_groups(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
-              const int32_t* __restrict__ sel_idx, int32_t* __restrict__ uni, int32_t* __restrict__ upre,
-              int32_t* __restrict__ gcount, int32_t* __restrict__ gtiles) {
+              const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ grows, int32_t* __restrict__ uni,
+              int32_t* __restrict__ upre, int32_t* __restrict__ gcount, int32_t* __restrict__ gtiles) {
     __shared__ int mask[4096];
     __shared__ int wsum[2][kPlanThreads / 64];
     const int grp = blockIdx.x, tid = threadIdx.x;
     const int gph = groups_per_head(g);
-    const int h = grp / gph, i0 = (grp % gph) * R;
+    const int h = grp / gph;
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
     const int NB = NBh + g.NBc;
@@ -284,8 +389,8 @@ k_plan_groups(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restr
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int i = i0 + r;
-        if (i >= g.NQB) break;
+        const int i = grows[grp * R + r];
+        if (i >= g.NQB) continue;
         const int row = h * g.NQB + i;
         const int c = sel_count[row];
         const int32_t* ids = sel_idx + (size_t)row * g.NB_max;
@@ -342,8 +447,9 @@ __global__ void __launch_bounds__(1024) k_plan_scan(int NG, const int32_t* __res
 // ---- attention ---------------------------------------------------------------
 
 struct PlanArgs {
-    float* part_o;     // [G][2][NW][DT][64 lanes][16]: unnormalised O of split groups
-    float2* part_ml;   // [G][2][NW][64 lanes]: (running max, lane's row-sum share)
+    float* part_o;          // [G][2][NW][DT][64 lanes][16]: unnormalised O of split groups
+    float2* part_ml;        // [G][2][NW][64 lanes]: (running max, lane's row-sum share)
+    const int32_t* grows;   // [NG][R]: rows of each group (NQB past the head's rows)
     int NG, G;
 };
 
@@ -480,7 +586,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         // one group per pass: its tiles [n, end) of this range, with the ring
         // refilled from the first buffer (a pipeline drain per group change)
         const int grp = pg;
-        const int h = grp / gph, i = (grp % gph) * R + myr;
+        const int h = grp / gph, i = pl.grows[grp * R + myr];
         const int S = gstart[grp], Tg = gtiles[grp];
         const int end = (S + Tg < a1 ? S + Tg : a1) - a0;
         const long long hoff = (long long)h * D;
@@ -572,7 +678,7 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
     }
     const int gph = groups_per_head(g);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int h = grp / gph, i = (grp % gph) * R + (wave >> 1);
+    const int h = grp / gph, i = pl.grows[grp * R + (wave >> 1)];
     Wave<D> w;
     start_rows<D>(g, q, h, i, w);
     if (Tg > 0) {
@@ -620,7 +726,7 @@ int sparse_wgs() {
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SparseWs {
-    int32_t *uni, *upre, *gcount, *gtiles, *gstart;
+    int32_t *grows, *uni, *upre, *gcount, *gtiles, *gstart;
     float* part_o;
     float2* part_ml;
 };
@@ -633,6 +739,7 @@ SparseWs carve(const Geo& g, void* ws) {
     const int NG = n_groups(g);
     char* p = (char*)ws;
     SparseWs s;
+    s.grows = (int32_t*)p;   p += al256((size_t)NG * R * 4);
     s.uni = (int32_t*)p;     p += al256((size_t)NG * g.NB_max * 4);
     s.upre = (int32_t*)p;    p += al256((size_t)NG * g.NB_max * 4);
     s.gcount = (int32_t*)p;  p += al256((size_t)NG * 4);
@@ -647,8 +754,8 @@ SparseWs carve(const Geo& g, void* ws) {
 
 size_t sparse_bf16_ws_bytes(const Geo& g) {
     const int NG = n_groups(g);
-    return 2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) + al256((size_t)(NG + 1) * 4) +
-           part_o_bytes(g) + part_ml_bytes();
+    return al256((size_t)NG * R * 4) + 2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) +
+           al256((size_t)(NG + 1) * 4) + part_o_bytes(g) + part_ml_bytes();
 }
 
 template <int D>
@@ -658,10 +765,11 @@ static void launch_d(const Geo& g, const void* q, const void* k_hist, const void
                      hipStream_t st) {
     const int NG = n_groups(g);
     const SparseWs s = carve(g, ws);
+    hipLaunchKernelGGL(k_plan_rows, dim3(g.H), dim3(kGroupThreads), 0, st, g, n_sel, sel_count, sel_idx, s.grows);
     hipLaunchKernelGGL(k_plan_groups, dim3(NG), dim3(kPlanThreads), 0, st, g, n_sel, sel_count, sel_idx,
-                       s.uni, s.upre, s.gcount, s.gtiles);
+                       (const int32_t*)s.grows, s.uni, s.upre, s.gcount, s.gtiles);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, NG, (const int32_t*)s.gtiles, s.gstart);
-    PlanArgs pl{s.part_o, s.part_ml, NG, sparse_wgs()};
+    PlanArgs pl{s.part_o, s.part_ml, s.grows, NG, sparse_wgs()};
     const int per_xcd = (pl.G + 7) / 8;
     hipLaunchKernelGGL((k_sparse_attn32<D>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
                        (const bf16_t*)k_hist, (const bf16_t*)v_hist, (const bf16_t*)k_intra,
