@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -80,6 +82,20 @@ int done() {
         return HSAKV_ERR_HIP;
     }
     return HSAKV_OK;
+}
+
+// A second stream per device (default priority, created on first use and
+// kept until the process ends) for work that can run beside the caller's
+// stream. nullptr if it cannot be created: the caller then stays on its own
+// stream.
+hipStream_t side_stream() {
+    static std::mutex mu;
+    static hipStream_t tab[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!tab[dev] && hipStreamCreateWithFlags(&tab[dev], hipStreamNonBlocking) != hipSuccess) tab[dev] = nullptr;
+    return tab[dev];
 }
 
 // ---- workspace sizes -------------------------------------------------------
@@ -405,10 +421,24 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
         run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                            nullptr, qb, kb, st);
+        // The sparse plan needs the selection only: it runs on a side stream
+        // beside the low-rank branch, and the attention waits for both.
+        hipStream_t side = side_stream();
+        hipEvent_t fork = nullptr, join = nullptr;
+        const bool split = side && side != st &&
+                           hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
+                           hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
+                           hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
+        launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, sparse_ws, split ? side : st);
+        const bool joined = split && hipEventRecord(join, side) == hipSuccess;
         run_linear<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
                            in->F, o_linear, nullptr, nullptr, c, st);
-        launch_sparse_attn<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,
-                                   sel_count, sel_idx, sparse_ws, ep, st);
+        if (joined) (void)hipStreamWaitEvent(st, join, 0);
+        else if (split) (void)hipStreamSynchronize(side);   // plan enqueued but not joined: finish it
+        launch_sparse_compute_bf16(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, sparse_ws, ep,
+                                   st);
+        if (fork) (void)hipEventDestroy(fork);
+        if (join) (void)hipEventDestroy(join);
     } else {
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, st);

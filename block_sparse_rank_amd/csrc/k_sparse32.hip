@@ -276,96 +276,156 @@ HSAKV_DEV int block_excl_scan(int v, int* tot, int* wsum) {
 // not yet grouped and takes, R - 1 times, the remaining row whose selection
 // shares the most tiles with the group's union less the tiles it would add.
 // grows[grp * R + r] = row (NQB past the head's rows). Heads with more than
-// kGroupThreads rows or more than 32 kGroupWords blocks keep consecutive
-// rows. The grouping only orders the work: each row's result is the same.
-constexpr int kGroupWords = 16;
-constexpr int kGroupThreads = 256;
+// 64 kGroupRowsPerLane rows or more than 32 kGroupWords tiles keep
+// consecutive rows. The grouping only orders the work: each row's result is
+// the same.
+constexpr int kGroupWords = 32;       // bitmask words per row (tiles per head <= 1024)
+constexpr int kGroupRowsPerLane = 2;  // rows per lane (rows per head <= 128)
 
-// Tiles of the blocks in word w of a selection bitmask (bit b of word w is
-// block 32 w + b; blocks below NBh are history blocks).
-HSAKV_DEV int mask_tiles(uint32_t x, int w, int NBh, int th, int tc) {
-    const int lo = 32 * w;
-    const uint32_t hm = lo + 32 <= NBh ? ~0u : (lo >= NBh ? 0u : (1u << (NBh - lo)) - 1u);
-    return th * __builtin_popcount(x & hm) + tc * __builtin_popcount(x & ~hm);
+// Tiles of the head's key blocks, history blocks first: block b < NBh covers
+// tiles [th b, th (b + 1)), chunk block NBh + c covers th NBh + tc c onwards.
+HSAKV_DEV int tiles_of_head(const Geo& g, int NBh, int& th, int& tc) {
+    th = (g.Binter + KT - 1) / KT;
+    tc = (g.Bintra + KT - 1) / KT;
+    return th * NBh + tc * g.NBc;
 }
 
-// Largest key over the work-group (all threads get it).
-HSAKV_DEV unsigned long long block_max(unsigned long long key, unsigned long long* red) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long t = __shfl_xor(key, o, 64);
-        key = t > key ? t : key;
-    }
-    if (lane == 0) red[wv] = key;
-    __syncthreads();
-    unsigned long long m = red[0];
-#pragma unroll
-    for (int i = 1; i < kGroupThreads / 64; ++i) m = red[i] > m ? red[i] : m;
-    __syncthreads();
-    return m;
-}
-
-__global__ void __launch_bounds__(kGroupThreads)
-k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
-            const int32_t* __restrict__ sel_idx, int32_t* __restrict__ grows) {
-    __shared__ uint32_t bits_s[kGroupThreads][kGroupWords];
-    __shared__ uint32_t uni_s[kGroupWords];
-    __shared__ unsigned long long red[kGroupThreads / 64];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    const int gph = groups_per_head(g);
+// Selection of one row as a tile bitmask: work-group (h, i) writes
+// tbits[(h NQB + i) kGroupWords + w], bit t % 32 of word t / 32 set when the
+// row selected the block of tile t.
+__global__ void __launch_bounds__(64)
+k_plan_bits(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
+            const int32_t* __restrict__ sel_idx, uint32_t* __restrict__ tbits) {
+    __shared__ uint32_t words[kGroupWords];
+    const int row = blockIdx.x, lane = threadIdx.x;
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
     const int NB = NBh + g.NBc;
+    int th, tc;
+    if (tiles_of_head(g, NBh, th, tc) > 32 * kGroupWords) return;
+    if (lane < kGroupWords) words[lane] = 0u;
+    __syncthreads();
+    const int c = sel_count[row];
+    const int32_t* ids = sel_idx + (size_t)row * g.NB_max;
+    for (int j = lane; j < c; j += 64) {
+        const int b = ids[j];
+        if (b < 0 || b >= NB) continue;
+        const int t0 = b < NBh ? th * b : th * NBh + tc * (b - NBh);
+        const int nt = b < NBh ? th : tc;
+        for (int t = t0; t < t0 + nt; ++t) atomicOr(&words[t >> 5], 1u << (t & 31));
+    }
+    __syncthreads();
+    if (lane < kGroupWords) tbits[(size_t)row * kGroupWords + lane] = words[lane];
+}
+
+// Largest value over the wave, in every lane: DPP rotations within each row
+// of 16 lanes, then the row pairs (lanes l, l ^ 16) and halves (l, l ^ 32)
+// through the gfx950 lane swaps.
+HSAKV_DEV uint32_t wave_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));   // row_ror:8
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));   // row_ror:4
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));   // row_ror:2
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));   // row_ror:1
+    const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = mx(s16[0], s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return mx(s32[0], s32[1]);
+}
+
+// One work-group per head, kGroupWaves waves: lane l of every wave holds rows
+// l and l + 64, wave v holds words [kWordsPerWave v, kWordsPerWave (v + 1))
+// of their bitmasks. The waves sum their partial overlaps through LDS; every
+// wave then takes the same pick.
+constexpr int kGroupWaves = 4;
+constexpr int kWordsPerWave = kGroupWords / kGroupWaves;
+
+__global__ void __launch_bounds__(64 * kGroupWaves)
+k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restrict__ tbits,
+            int32_t* __restrict__ grows) {
+    __shared__ int part[2][kGroupWaves][64 * kGroupRowsPerLane];
+    const int h = blockIdx.x, lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int gph = groups_per_head(g);
+    const int n_sel = *n_sel_p;
+    const int NBh = hist_blocks(g, n_sel);
+    int th, tc;
+    const int NT = tiles_of_head(g, NBh, th, tc);
     int32_t* out = grows + (size_t)h * gph * R;
-    if (NB > 32 * kGroupWords || g.NQB > kGroupThreads) {
-        for (int e = tid; e < gph * R; e += kGroupThreads) out[e] = e < g.NQB ? e : g.NQB;
+    if (NT > 32 * kGroupWords || g.NQB > 64 * kGroupRowsPerLane) {
+        for (int e = threadIdx.x; e < gph * R; e += 64 * kGroupWaves) out[e] = e < g.NQB ? e : g.NQB;
         return;
     }
-    const int th = (g.Binter + KT - 1) / KT, tc = (g.Bintra + KT - 1) / KT;
-    for (int e = tid; e < kGroupThreads * kGroupWords; e += kGroupThreads) (&bits_s[0][0])[e] = 0u;
-    __syncthreads();
-    for (int r = 0; r < g.NQB; ++r) {
-        const int c = sel_count[h * g.NQB + r];
-        const int32_t* ids = sel_idx + (size_t)(h * g.NQB + r) * g.NB_max;
-        for (int j = tid; j < c; j += kGroupThreads) {
-            const int b = ids[j];
-            if (b >= 0 && b < NB) atomicOr(&bits_s[r][b >> 5], 1u << (b & 31));
-        }
-    }
-    __syncthreads();
-    // thread tid holds row tid
-    uint32_t bits[kGroupWords];
-    int own = 0;
+    const int W = (NT + 31) >> 5;
+    uint32_t bits[kGroupRowsPerLane][kWordsPerWave];
+    bool left[kGroupRowsPerLane];
 #pragma unroll
-    for (int w = 0; w < kGroupWords; ++w) {
-        bits[w] = bits_s[tid][w];
-        own += mask_tiles(bits[w], w, NBh, th, tc);
+    for (int k = 0; k < kGroupRowsPerLane; ++k) {
+        const int row = lane + 64 * k;
+        left[k] = row < g.NQB;
+        const uint32_t* src = tbits + (size_t)(h * g.NQB + (left[k] ? row : 0)) * kGroupWords;
+        int cnt = 0;
+#pragma unroll
+        for (int x = 0; x < kWordsPerWave; ++x) {
+            const int w = kWordsPerWave * wv + x;
+            bits[k][x] = left[k] && w < W ? src[w] : 0u;
+            cnt += __builtin_popcount(bits[k][x]);
+        }
+        part[1][wv][row] = cnt;
     }
-    bool left = tid < g.NQB;
-    const unsigned long long lowrow = 0xffffffffull - (unsigned)tid;
+    __syncthreads();
+    int own[kGroupRowsPerLane];
+#pragma unroll
+    for (int k = 0; k < kGroupRowsPerLane; ++k) {
+        own[k] = 0;
+#pragma unroll
+        for (int v = 0; v < kGroupWaves; ++v) own[k] += part[1][v][lane + 64 * k];
+    }
+    uint32_t uni[kWordsPerWave];
+#pragma unroll
+    for (int x = 0; x < kWordsPerWave; ++x) uni[x] = 0u;
+    int buf = 0;
     for (int j = 0; j < gph; ++j) {
         for (int r = 0; r < R; ++r) {
-            unsigned long long key = 0;
-            if (left) {
-                int score = 0;   // the group's first row: the lowest remaining
+            // partial overlaps of this wave's words with the group's union
+            if (r > 0) {
+#pragma unroll
+                for (int k = 0; k < kGroupRowsPerLane; ++k) {
+                    int ov = 0;
+#pragma unroll
+                    for (int x = 0; x < kWordsPerWave; ++x) ov += __builtin_popcount(bits[k][x] & uni[x]);
+                    part[buf][wv][lane + 64 * k] = ov;
+                }
+                __syncthreads();
+            }
+            // key: score (shared tiles less added tiles) above the lowest row
+            uint32_t key = 0;
+#pragma unroll
+            for (int k = 0; k < kGroupRowsPerLane; ++k) {
+                if (!left[k]) continue;
+                int score = 0;
                 if (r > 0) {
                     int ov = 0;
 #pragma unroll
-                    for (int w = 0; w < kGroupWords; ++w) ov += mask_tiles(bits[w] & uni_s[w], w, NBh, th, tc);
-                    score = 2 * ov - own;   // shared tiles less the tiles it adds
+                    for (int v = 0; v < kGroupWaves; ++v) ov += part[buf][v][lane + 64 * k];
+                    score = 2 * ov - own[k];
                 }
-                key = ((unsigned long long)(unsigned)(score + (1 << 20)) << 32) | lowrow;
+                const uint32_t kk = ((uint32_t)(score + 4096) << 8) | (uint32_t)(255 - (lane + 64 * k));
+                key = kk > key ? kk : key;
             }
-            const unsigned long long m = block_max(key, red);
-            const int pick = m ? (int)(0xffffffffu - (unsigned)(m & 0xffffffffull)) : g.NQB;
-            if (tid == 0) out[j * R + r] = pick;
-            if (m && pick == tid) {
-                left = false;
+            key = wave_max_u32(key);
+            if (r > 0) buf ^= 1;
+            const int pick = key ? 255 - (int)(key & 255u) : g.NQB;
+            if (threadIdx.x == 0) out[j * R + r] = pick;
+            if (!key) continue;
+            const int pl_ = pick & 63, pk = pick >> 6;
 #pragma unroll
-                for (int w = 0; w < kGroupWords; ++w) uni_s[w] = r == 0 ? bits[w] : (uni_s[w] | bits[w]);
+            for (int x = 0; x < kWordsPerWave; ++x) {
+                const uint32_t v = pk ? bits[1][x] : bits[0][x];
+                const uint32_t bw = (uint32_t)__builtin_amdgcn_readlane((int)v, pl_);
+                uni[x] = r == 0 ? bw : (uni[x] | bw);
             }
-            __syncthreads();
+            if (lane == pl_) left[pk] = false;
         }
     }
 }
@@ -726,6 +786,7 @@ int sparse_wgs() {
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SparseWs {
+    uint32_t* tbits;
     int32_t *grows, *uni, *upre, *gcount, *gtiles, *gstart;
     float* part_o;
     float2* part_ml;
@@ -739,6 +800,7 @@ SparseWs carve(const Geo& g, void* ws) {
     const int NG = n_groups(g);
     char* p = (char*)ws;
     SparseWs s;
+    s.tbits = (uint32_t*)p;  p += al256((size_t)g.H * g.NQB * kGroupWords * 4);
     s.grows = (int32_t*)p;   p += al256((size_t)NG * R * 4);
     s.uni = (int32_t*)p;     p += al256((size_t)NG * g.NB_max * 4);
     s.upre = (int32_t*)p;    p += al256((size_t)NG * g.NB_max * 4);
@@ -754,21 +816,32 @@ SparseWs carve(const Geo& g, void* ws) {
 
 size_t sparse_bf16_ws_bytes(const Geo& g) {
     const int NG = n_groups(g);
-    return al256((size_t)NG * R * 4) + 2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) +
+    return al256((size_t)g.H * g.NQB * kGroupWords * 4) + al256((size_t)NG * R * 4) +
+           2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) +
            al256((size_t)(NG + 1) * 4) + part_o_bytes(g) + part_ml_bytes();
 }
 
-template <int D>
-static void launch_d(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
-                     const void* k_intra, const void* v_intra, const int32_t* n_sel,
-                     const int32_t* sel_count, const int32_t* sel_idx, void* ws, const Epi& ep,
-                     hipStream_t st) {
+// The plan: it depends on the selection only, so a caller may run it beside
+// other work and order the compute part after it.
+void launch_sparse_plan_bf16(const Geo& g, const int32_t* n_sel, const int32_t* sel_count,
+                             const int32_t* sel_idx, void* ws, hipStream_t st) {
     const int NG = n_groups(g);
     const SparseWs s = carve(g, ws);
-    hipLaunchKernelGGL(k_plan_rows, dim3(g.H), dim3(kGroupThreads), 0, st, g, n_sel, sel_count, sel_idx, s.grows);
+    hipLaunchKernelGGL(k_plan_bits, dim3(g.H * g.NQB), dim3(64), 0, st, g, n_sel, sel_count, sel_idx, s.tbits);
+    hipLaunchKernelGGL(k_plan_rows, dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel, (const uint32_t*)s.tbits,
+                       s.grows);
     hipLaunchKernelGGL(k_plan_groups, dim3(NG), dim3(kPlanThreads), 0, st, g, n_sel, sel_count, sel_idx,
                        (const int32_t*)s.grows, s.uni, s.upre, s.gcount, s.gtiles);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, NG, (const int32_t*)s.gtiles, s.gstart);
+}
+
+namespace {
+
+template <int D>
+void launch_compute_d(const Geo& g, const void* q, const void* k_hist, const void* v_hist, const void* k_intra,
+                      const void* v_intra, const int32_t* n_sel, void* ws, const Epi& ep, hipStream_t st) {
+    const int NG = n_groups(g);
+    const SparseWs s = carve(g, ws);
     PlanArgs pl{s.part_o, s.part_ml, s.grows, NG, sparse_wgs()};
     const int per_xcd = (pl.G + 7) / 8;
     hipLaunchKernelGGL((k_sparse_attn32<D>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
@@ -780,12 +853,22 @@ static void launch_d(const Geo& g, const void* q, const void* k_hist, const void
                        (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl, ep);
 }
 
+}  // namespace
+
+// Attention and combine over a plan already in ws (launch_sparse_plan_bf16).
+void launch_sparse_compute_bf16(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
+                                const void* k_intra, const void* v_intra, const int32_t* n_sel, void* ws,
+                                const Epi& ep, hipStream_t st) {
+    if (g.d == 128)
+        launch_compute_d<128>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, ws, ep, st);
+    else
+        launch_compute_d<64>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, ws, ep, st);
+}
+
 void launch_sparse_attn_bf16_mfma32(const Geo& g, const void* q, const void* k_hist,
                                     const void* v_hist, const void* k_intra, const void* v_intra,
                                     const int32_t* n_sel, const int32_t* sel_count,
                                     const int32_t* sel_idx, void* ws, const Epi& ep, hipStream_t st) {
-    if (g.d == 128)
-        launch_d<128>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ws, ep, st);
-    else
-        launch_d<64>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count, sel_idx, ws, ep, st);
+    launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, ws, st);
+    launch_sparse_compute_bf16(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, ws, ep, st);
 }

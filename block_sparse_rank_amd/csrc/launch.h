@@ -44,6 +44,13 @@ void launch_sparse_attn_bf16_mfma32(const Geo&, const void* q, const void* k_his
                                     const void* k_intra, const void* v_intra, const int32_t* n_sel,
                                     const int32_t* sel_count, const int32_t* sel_idx, void* ws,
                                     const Epi& ep, hipStream_t);
+// the same in two parts: the plan (selection only) and, ordered after it,
+// the attention and combine
+void launch_sparse_plan_bf16(const Geo&, const int32_t* n_sel, const int32_t* sel_count, const int32_t* sel_idx,
+                             void* ws, hipStream_t);
+void launch_sparse_compute_bf16(const Geo&, const void* q, const void* k_hist, const void* v_hist,
+                                const void* k_intra, const void* v_intra, const int32_t* n_sel, void* ws,
+                                const Epi& ep, hipStream_t);
 template <typename T>
 void launch_lowrank_attn(const Geo&, const void* q, const void* k_hi, const void* v_hi, const void* k_lo,
                          const void* v_lo, const Epi& ep, hipStream_t);
