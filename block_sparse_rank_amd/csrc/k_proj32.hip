@@ -254,9 +254,20 @@ bool proj32_eligible(const Geo& g) {
     return g.elt == 2 && g.Tp % 8 == 0 && g.Lq % 8 == 0 && g.L % 8 == 0 && g.HD % BN == 0;
 }
 
+// Splits per tile: as many work-groups as are resident at once (two per CU)
+// and no more, so no work-group waits for a second round.
 int proj32_splits(const Geo& g) {
+    static int cache[64] = {0};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && cache[dev] > 0) {
+        cus = cache[dev];
+    } else {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 256;
+        if (dev >= 0 && dev < 64) cache[dev] = cus;
+    }
     const int tiles = 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
-    int s = (512 + tiles - 1) / tiles;
+    const int s = 2 * cus / tiles;
     return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
