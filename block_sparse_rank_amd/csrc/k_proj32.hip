@@ -13,6 +13,8 @@
 // (r x H*d), so it is split along k; each split writes an f32 partial and a
 // separate pass adds the partials in split order.
 //
+// Two tile shapes. For r >= 128 and H*d a multiple of 256: 256 x 256 tiles
+// (k_lowrank_proj256, below). Otherwise:
 // Work-group = 4 waves, tile 128 (m) x 128 (n), k-step 64. Wave w computes
 // rows 64(w%2).. and columns 64(w/2).. with four 32x32 accumulators. Tiles
 // are brought into LDS by global -> LDS DMA (two buffers, the next k-step in
@@ -246,6 +248,258 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
             }
 }
 
+// ---- 256 x 256 tiles ---------------------------------------------------------
+//
+// For r >= 128 and H*d a multiple of 256 the output tile is 256 (m) x 256 (n)
+// with 32-wide k-steps: a k-step reads E's slice once per 256 columns of
+// keys and each key slice once per 256 rows of E (half and a quarter of the
+// L2 reads of 128 x 128 tiles), 8 waves (wave w: rows 128 (w % 2), columns
+// 64 (w / 2), eight 32x32 accumulators), one work-group per CU and a ring of
+// four LDS stages, three in flight, so the stream keeps enough bytes in
+// flight. Rows are padded for conflict-free operand reads: X 5 slots (80 B,
+// the 16 rows of one b128 read phase on distinct banks), Y 36 slots (576 B).
+//
+// The k-steps of a split run over its history part, then its chunk part, each
+// ending in a partial step, so no step straddles the seam. The DMA goes
+// through buffer loads whose resource covers exactly the valid bytes: a Y row
+// past the part's end, or an X column past the end of E, is out of range and
+// not read; its LDS row is zeroed before use.
+constexpr int WM = 256, WN = 256, WK = 32, WT = 512, WWV = 8, WSTAGES = 4;
+constexpr int WA_SLOTS = WK / 8 + 1;           // 5
+constexpr int WB_SLOTS = WN / 8 + 4;           // 36
+constexpr int WA_ROWB = WA_SLOTS * 16;         // 80
+constexpr int WB_ROWB = WB_SLOTS * 16;         // 576
+constexpr int WA_BYTES = WM * WA_ROWB;         // 20480
+constexpr int WB_BYTES = WK * WB_ROWB;         // 18432
+constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 38912; four stages 155648 bytes
+constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 20
+constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 18
+constexpr int W_PER = 5;                       // DMA instructions per wave and k-step
+constexpr int W_SPARE = 2048;                  // LDS target of the two idle instructions
+static_assert(WM * WA_SLOTS % 64 == 0 && WK * WB_SLOTS % 64 == 0, "whole wave instructions");
+static_assert(WA_BYTES == WA_INSTR * 1024, "Y follows X in instruction order");
+static_assert(WA_INSTR + WB_INSTR + 2 == WWV * W_PER, "38 DMA instructions plus two idle ones");
+
+// Raw buffer resource: base p, `bytes` in range, 32-bit untyped data.
+HSAKV_DEV __amdgpu_buffer_rsrc_t w_rsrc(const bf16_t* p, long long bytes) {
+    const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), 0, n, 0x00020000);
+}
+
+// The LDS destination of a DMA as an address the compiler cannot trace to the
+// ring: the kernel orders each DMA before the reads of its stage (a vmcnt
+// wait, then the barrier), and the compiler's own tracking of LDS DMA targets
+// would add waits that drain the prefetch too.
+HSAKV_DEV lds_void_t* w_dst(char* p) {
+    const uint32_t v = (uint32_t)(uintptr_t)(lds_void_t*)p;
+    return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
+}
+
+template <int N>
+HSAKV_DEV void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// LDS-only work-group barrier (DMA in flight stays in flight).
+HSAKV_DEV void w_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Byte offsets of this wave's DMA instructions j = wave + 8 q (fixed over
+// the k-steps): X (j < 20) m * L + 8 * slot from the step's first column,
+// Y (20 <= j < 38) row * HD + n0 + 8 * slot from the step's first row; pad
+// lanes load slot 0 of their row.
+HSAKV_DEV void w_lanes(uint32_t (&off)[W_PER], const Geo& g, int wave, int m0, int n0) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < W_PER; ++q) {
+        const int j = wave + WWV * q;
+        const int La = j * 64 + lane, Lb = (j - WA_INSTR) * 64 + lane;
+        const int ra = La / WA_SLOTS, sa = La % WA_SLOTS, rb = Lb / WB_SLOTS, sb = Lb % WB_SLOTS;
+        const int m = m0 + ra < g.r ? m0 + ra : g.r - 1;
+        const uint32_t oa = 2u * (uint32_t)(m * (int)g.L + (sa < WK / 8 ? sa : 0) * 8);
+        const uint32_t ob = 2u * (uint32_t)(rb * g.HD + n0 + (sb < WN / 8 ? sb : 0) * 8);
+        off[q] = j < WA_INSTR ? oa : (j < WA_INSTR + WB_INSTR ? ob : 0u);
+    }
+}
+
+// Zero the Y rows [first, WK) of a stage.
+HSAKV_DEV void w_zero_tail(char* buf, int first) {
+    for (int idx = threadIdx.x; idx < (WK - first) * (WN / 8); idx += WT) {
+        const int row = first + idx / (WN / 8), c = idx % (WN / 8);
+        *reinterpret_cast<uint4*>(buf + WA_BYTES + row * WB_ROWB + c * 16) = uint4{0, 0, 0, 0};
+    }
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned w_u32x2_t;
+
+// One k-step of MFMA work. The eight transpose reads of Y sit in one asm
+// block that waits for them itself: issued as builtins, they would make the
+// compiler wait for every DMA in flight first (the next steps included).
+HSAKV_DEV void w_compute(const char* buf, f32x16_t (&acc)[4][2], int wave) {
+    const int lane = threadIdx.x & 63;
+    const int mw = wave & 1, nw = wave >> 1;
+    const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
+    const char* A = buf + (128 * mw + r32) * WA_ROWB + 16 * g2;
+    const char* B = buf + WA_BYTES + (8 * (G >> 1) + (j >> 2)) * WB_ROWB + (64 * nw + 16 * (G & 1) + 4 * (j & 3)) * 2;
+    const uint32_t bb = (uint32_t)(uintptr_t)(const lds_i16x4_t*)B;
+    // r[4 kk + 2 nt + h]: k rows 16 kk + 4 h (+ 8 (G / 2) + j / 4), columns 32 nt + ...
+    constexpr int H = 4 * WB_ROWB, K1 = 16 * WB_ROWB;
+    bf16x8_t a0[4], a1[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) a0[mt] = *reinterpret_cast<const bf16x8_t*>(A + 32 * mt * WA_ROWB);
+    w_u32x2_t r[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(bb), "i"(H), "i"(64), "i"(64 + H), "i"(K1), "i"(K1 + H), "i"(K1 + 64), "i"(K1 + 64 + H)
+        : "memory");
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) a1[mt] = *reinterpret_cast<const bf16x8_t*>(A + 32 * mt * WA_ROWB + 32);
+    bf16x8_t b[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            b[kk][nt] = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(r[4 * kk + 2 * nt], r[4 * kk + 2 * nt + 1], 0, 1, 2, 3));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[mt], b[0][nt], acc[mt][nt], 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[mt], b[1][nt], acc[mt][nt], 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(WT, 1)
+k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__ F,
+                  const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+                  const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
+                  const int32_t* __restrict__ n_sel_p, int nsplit, int per_xcd, float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) char ring[WSTAGES * WSTAGE + W_SPARE];
+    const int MT = (g.r + WM - 1) / WM, NTL = g.HD / WN;
+    const int total = nsplit * 2 * MT * NTL;
+    const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (lin >= total) return;
+    const int nt_i = lin % NTL;
+    const int mt_i = (lin / NTL) % MT;
+    const int z = (lin / (NTL * MT)) & 1;
+    const int split = lin / (NTL * MT * 2);
+    const int m0 = mt_i * WM, n0 = nt_i * WN;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bf16_t* X = z ? F : E;
+    const bf16_t* Yh = z ? v_hist : k_hist;
+    const bf16_t* Yc = z ? v_intra : k_intra;
+
+    // The split's k-steps: nh over its history part [kb, he), then the rest
+    // over its chunk part [cb, ke) (k counted over the active rows).
+    const long long Lh = (long long)(*n_sel_p) * g.Tp;
+    const long long Lact = Lh + g.Lq;
+    const long long per = ((g.L + nsplit - 1) / nsplit + WK - 1) / WK * WK;
+    const long long kb = (long long)split * per;
+    const long long ke = kb + per < Lact ? kb + per : Lact;
+    const long long he = ke < Lh ? ke : Lh;
+    const long long cb = kb > Lh ? kb : Lh;
+    const int nh = kb < he ? (int)((he - kb + WK - 1) / WK) : 0;
+    const int n = nh + (cb < ke ? (int)((ke - cb + WK - 1) / WK) : 0);
+
+    uint32_t off[W_PER];
+    w_lanes(off, g, wave, m0, n0);
+    const __amdgpu_buffer_rsrc_t r_idle = w_rsrc(X, 0);
+    const long long xbytes = 2LL * g.r * g.L;
+
+    // Send k-step s into its ring stage: per instruction a uniform resource
+    // (X, Y or the empty one of the idle instructions) and LDS target.
+    auto send = [&](int s) __attribute__((always_inline)) {
+        if (s >= n) return;
+        const bool hist = s < nh;
+        const long long k = hist ? kb + (long long)s * WK : cb + (long long)(s - nh) * WK;
+        const long long end = hist ? he : ke;
+        const long long col = hist ? k : g.hist_rows + (k - Lh);
+        const bf16_t* yb = hist ? Yh + k * g.HD : Yc + (k - Lh) * g.HD;
+        const int rows = end - k < WK ? (int)(end - k) : WK;
+        const __amdgpu_buffer_rsrc_t rx = w_rsrc(X + col, xbytes - 2 * col);
+        const __amdgpu_buffer_rsrc_t ry = w_rsrc(yb, 2LL * rows * g.HD);
+        char* buf = ring + (s & 3) * WSTAGE;
+#pragma unroll
+        for (int q = 0; q < W_PER; ++q) {
+            const int j = wave + WWV * q;
+            const __amdgpu_buffer_rsrc_t rs = j < WA_INSTR ? rx : (j < WA_INSTR + WB_INSTR ? ry : r_idle);
+            char* dst = j < WA_INSTR + WB_INSTR ? buf + j * 1024 : ring + WSTAGES * WSTAGE + (j & 1) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, w_dst(dst), 16, off[q], 0, 0, 0);
+        }
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16_t{};
+
+    send(0);
+    send(1);
+    send(2);
+#pragma unroll 1
+    for (int i = 0; i < n; ++i) {
+        // step i has landed once only the steps sent after it are outstanding
+        const int later = (n < i + 3 ? n : i + 3) - i - 1;
+        if (later >= 2)
+            wait_vm<2 * W_PER>();
+        else if (later == 1)
+            wait_vm<W_PER>();
+        else
+            wait_vm<0>();
+        w_barrier();
+        char* now = ring + (i & 3) * WSTAGE;
+        const bool hist = i < nh;
+        const long long k = hist ? kb + (long long)i * WK : cb + (long long)(i - nh) * WK;
+        const long long end = hist ? he : ke;
+        if (end - k < WK) {   // the last, partial step of a part
+            w_zero_tail(now, (int)(end - k));
+            w_barrier();
+        }
+        send(i + 3);
+        w_compute(now, acc, wave);
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int mw = wave & 1, nw = wave >> 1, g2 = lane >> 5;
+    float* out = part + (size_t)(split * 2 + z) * g.r * g.HD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + 128 * mw + 32 * mt + 8 * (e >> 2) + 4 * g2 + (e & 3);
+                const int nn = n0 + 64 * nw + 32 * nt + (lane & 31);
+                if (m < g.r) out[(size_t)m * g.HD + nn] = acc[mt][nt][e];
+            }
+}
+
+// CUs of the current device (cached per device).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+bool big_tiles(const Geo& g) { return g.r >= 128 && g.HD % WN == 0; }
+
 }  // namespace
 
 // The MFMA projection needs 16-byte aligned 8-element runs of E's columns
@@ -254,20 +508,19 @@ bool proj32_eligible(const Geo& g) {
     return g.elt == 2 && g.Tp % 8 == 0 && g.Lq % 8 == 0 && g.L % 8 == 0 && g.HD % BN == 0;
 }
 
-// Splits per tile: as many work-groups as are resident at once (two per CU)
-// and no more, so no work-group waits for a second round.
+// Splits per tile: as many work-groups as are resident at once (two per CU
+// with 128 x 128 tiles, one with 256 x 256) and no more, so no work-group
+// waits for a second round.
 int proj32_splits(const Geo& g) {
-    static int cache[64] = {0};
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && cache[dev] > 0) {
-        cus = cache[dev];
+    const int cus = device_cus();
+    int s;
+    if (big_tiles(g)) {
+        const int tiles = 2 * ((g.r + WM - 1) / WM) * (g.HD / WN);
+        s = cus / tiles;
     } else {
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-            cus = 256;
-        if (dev >= 0 && dev < 64) cache[dev] = cus;
+        const int tiles = 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
+        s = 2 * cus / tiles;
     }
-    const int tiles = 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
-    const int s = 2 * cus / tiles;
     return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
@@ -275,6 +528,14 @@ void launch_lowrank_proj32(const Geo& g, const void* E, const void* F, const voi
                            const void* v_hist, const void* k_intra, const void* v_intra,
                            const int32_t* n_sel, float* part, hipStream_t st) {
     const int ns = proj32_splits(g);
+    if (big_tiles(g)) {
+        const int total = ns * 2 * ((g.r + WM - 1) / WM) * (g.HD / WN);
+        const int per_xcd = (total + 7) / 8;
+        hipLaunchKernelGGL(k_lowrank_proj256, dim3(8 * per_xcd), dim3(WT), 0, st, g, (const bf16_t*)E,
+                           (const bf16_t*)F, (const bf16_t*)k_hist, (const bf16_t*)v_hist,
+                           (const bf16_t*)k_intra, (const bf16_t*)v_intra, n_sel, ns, per_xcd, part);
+        return;
+    }
     const int total = ns * 2 * ((g.r + BM - 1) / BM) * (g.HD / BN);
     const int per_xcd = (total + 7) / 8;
     hipLaunchKernelGGL(k_lowrank_proj32, dim3(8 * per_xcd), dim3(NT), 0, st, g, (const bf16_t*)E,

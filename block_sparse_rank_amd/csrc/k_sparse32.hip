@@ -152,7 +152,9 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sub][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // lanes l and l + 32 hold the two key halves of the same query
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     // the running max is raised only when a score passes it by more than
     // kLazyMax, so O is rarely rescaled; weights stay below 2^kLazyMax
     const float mt = mx * scale_log2;

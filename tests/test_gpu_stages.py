@@ -39,6 +39,16 @@ VARIANTS = [
                                clustered=True, tau_law="uniform", seed=19), {}),
     ("bf16-no-page", _variant("tiny", dtype="bf16", H=4, d=128, clustered=True,
                               tau_law="uniform", seed=20), dict(cur_prompt=9)),
+    # low-rank projection with 256 x 256 tiles (r >= 128, H*d a multiple of 256):
+    # rows past r inside a tile, a 32-key step across the history/chunk seam
+    ("bf16-r128-seam", _variant("tiny", dtype="bf16", H=2, d=128, r=128, Lq=200, tokens_per_frame=13,
+                                clustered=True, tau_law="uniform", seed=25), {}),
+    # two row tiles, the second ragged
+    ("bf16-r320-hd256", _variant("tiny", dtype="bf16", H=4, d=64, r=320, Lq=136, tokens_per_frame=13,
+                                 P=8, Kp=3, clustered=True, tau_law="uniform", seed=26), {}),
+    # six k-steps per split (the LDS ring wraps), a split across the seam
+    ("bf16-r128-long", _variant("tiny", dtype="bf16", H=2, d=128, r=128, Lq=1000, tokens_per_frame=100,
+                                clustered=True, tau_law="uniform", seed=27), {}),
 ]
 
 
