@@ -617,13 +617,23 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const int gph = groups_per_head(g);
 
-    // producer position: the next tile to send
-    int pg = last_le(gstart, pl.NG, a0);
-    const int first_grp = pg;
-    int pcnt = gcount[pg];
-    int pe = last_le(upre + (size_t)pg * g.NB_max, pcnt, a0 - gstart[pg]);
-    int pt = a0 - gstart[pg] - upre[(size_t)pg * g.NB_max + pe];
-    int pmask, pntile;
+    // The range holds pieces of consecutive groups: the tail of the first
+    // (its highest blocks) when the range starts inside it, whole groups, and
+    // the head of the last (its lowest blocks). A range that starts inside a
+    // group and runs past it takes the later groups first and that first
+    // tail last, so it sweeps the blocks from low to high indices, in step
+    // with the other ranges: the work-groups of an XCD then read nearby
+    // blocks at the same time and share them in L2.
+    const int g0 = last_le(gstart, pl.NG, a0);
+    const bool wrap = a0 > gstart[g0] && gstart[g0] + gtiles[g0] < a1;
+    auto next_group = [&](int p) __attribute__((always_inline)) -> int {
+        do {
+            ++p;
+        } while (p < pl.NG && gcount[p] == 0);
+        return p;
+    };
+    int pg = wrap ? next_group(g0) : g0;
+    int pe, pt, pmask, pntile;
     Cursor pc;
     auto load_entry = [&]() __attribute__((always_inline)) {
         const int v = uni[(size_t)pg * g.NB_max + pe];
@@ -631,7 +641,12 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         pc = open_block(g, NBh, Lh, v & 0xffff);
         pntile = (pc.len + KT - 1) / KT;
     };
-    load_entry();
+    // producer position: the tile `lo` (global sequence) of group pg
+    auto seek = [&](int lo) __attribute__((always_inline)) {
+        pe = last_le(upre + (size_t)pg * g.NB_max, gcount[pg], lo - gstart[pg]);
+        pt = lo - gstart[pg] - upre[(size_t)pg * g.NB_max + pe];
+        load_entry();
+    };
     // next tile of the same group (the caller knows one exists)
     auto advance = [&]() __attribute__((always_inline)) {
         if (++pt >= pntile) {
@@ -642,15 +657,18 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     };
 
     Wave<D> w;
-    int n = 0;        // tiles of the range computed
-    int issued = 0;   // tiles of the range sent
+    int done = 0;     // tiles of the range computed
     while (true) {
-        // one group per pass: its tiles [n, end) of this range, with the ring
+        // one group per pass: its tiles [lo, hi) of this range, with the ring
         // refilled from the first buffer (a pipeline drain per group change)
         const int grp = pg;
         const int h = grp / gph, i = pl.grows[grp * R + myr];
         const int S = gstart[grp], Tg = gtiles[grp];
-        const int end = (S + Tg < a1 ? S + Tg : a1) - a0;
+        const int lo = S > a0 ? S : a0, hi = S + Tg < a1 ? S + Tg : a1;
+        seek(lo);
+        const int end = hi - lo;
+        int n = 0;        // tiles of the piece computed
+        int issued = 0;   // tiles of the piece sent
         const long long hoff = (long long)h * D;
         start_rows<D>(g, q, h, i, w);
         // tile info for the consumer: row mask << 7 | valid keys
@@ -696,7 +714,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         if (S >= a0 && S + Tg <= a1) {
             finish_rows<D>(g, ep, h, i, w);
         } else {
-            const int slot = 2 * k + (grp == first_grp ? 0 : 1);
+            const int slot = 2 * k + (grp == g0 ? 0 : 1);
             const int lane = threadIdx.x & 63;
 #pragma unroll
             for (int dt = 0; dt < Wave<D>::DT; ++dt) {
@@ -707,15 +725,11 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
             }
             pl.part_ml[((size_t)slot * NW + wave) * 64 + lane] = float2{w.m, w.l};
         }
-        if (n == total) break;
-        // next group with tiles; every wave is done with the ring before it refills
-        pe = 0;
-        pt = 0;
-        do {
-            ++pg;
-            pcnt = gcount[pg];
-        } while (pcnt == 0);
-        load_entry();
+        done += end;
+        if (done == total) break;
+        // next piece; every wave is done with the ring before it refills
+        pg = next_group(pg);
+        if (wrap && (pg >= pl.NG || gstart[pg] >= a1)) pg = g0;
         lds_barrier();
     }
 }
