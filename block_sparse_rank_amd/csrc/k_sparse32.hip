@@ -77,12 +77,17 @@ struct Lay {
 
 // DMA one tile (64 key rows of K and V) into an LDS buffer. Rows past `nvalid`
 // (the ragged end of a block) load the last valid row: their scores are
-// masked to -inf, so P = 0 multiplies finite values.
+// masked to -inf, so P = 0 multiplies finite values. The DMA goes through
+// buffer loads (raw buffer, base = the tile's first row): the compiler counts
+// those as vector memory only, so the LDS operand reads that follow keep
+// exact lgkmcnt waits and can be issued ahead of their MFMAs (a pending
+// global_load_lds makes every LDS read wait for all earlier ones).
 template <int D>
-HSAKV_DEV void dma_tile(char* buf, const bf16_t* __restrict__ kb, const bf16_t* __restrict__ vb,
-                        int nvalid, int HD) {
+HSAKV_DEV void dma_tile(char* buf, const bf16_t* kb, const bf16_t* vb, int nvalid, int HD) {
     using LY = Lay<D>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kb), 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vb), 0, -1, 0x00020000);
 #pragma unroll
     for (int j = 0; j < LY::PER_WAVE; ++j) {
         const int slot0 = (wave * LY::PER_WAVE + j) * 64;
@@ -91,8 +96,8 @@ HSAKV_DEV void dma_tile(char* buf, const bf16_t* __restrict__ kb, const bf16_t* 
         const int rg = r < nvalid ? r : nvalid - 1;
         const int offk = rg * HD + ((sl ^ LY::swz_k(r)) << 3);
         const int offv = rg * HD + ((sl ^ LY::swz_v(r)) << 3);
-        __builtin_amdgcn_global_load_lds(kb + offk, (lds_void_t*)(buf + slot0 * 16), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + offv, (lds_void_t*)(buf + LY::MAT + slot0 * 16), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + slot0 * 16), 16, 2 * offk, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + LY::MAT + slot0 * 16), 16, 2 * offv, 0, 0, 0);
     }
 }
 
@@ -119,44 +124,28 @@ struct Wave {
     float m, l;                         // running max (log2 units), this lane's share of the row sum
 };
 
+// Online softmax over one 32-key half of a tile (keys 32 sub..): mask the
+// keys past `nvalid`, update the running max (raised only when a score
+// passes it by more than kLazyMax, so O is rarely rescaled; weights stay
+// below 2^kLazyMax) and the row sum, and turn the scores into weights.
 template <int D>
-HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid, float scale_log2) {
-    using LY = Lay<D>;
-    const int lane = threadIdx.x & 63;
-    const int r32 = lane & 31, g2 = lane >> 5;
-    f32x16_t s[2];
+HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float scale_log2) {
+    const int g2 = (threadIdx.x & 63) >> 5;
+    if (nvalid < 32 * (sub + 1)) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-        s[sub] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < Wave<D>::KS; ++ks) {
-            const int row = 32 * sub + r32;
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                kt + row * LY::ROWB + (((2 * ks + g2) ^ LY::swz_k(row)) << 4));
-            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w.qf[ks], s[sub], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * sub + 8 * (i >> 2) + 4 * g2 + (i & 3);
+            if (key >= nvalid) s[i] = -INFINITY;
         }
     }
-    // raw scores: the row max is taken before scaling (scale > 0), and the
-    // scale folds into the exponent's FMA
-    float mx = -INFINITY;
-    if (nvalid < KT) {
+    // raw scores: the max is taken before scaling (scale > 0), and the scale
+    // folds into the exponent's FMA
+    float mx = s[0];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = 32 * sub + 8 * (i >> 2) + 4 * g2 + (i & 3);
-                if (key >= nvalid) s[sub][i] = -INFINITY;
-            }
-    }
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sub][i]);
-    // lanes l and l + 32 hold the two key halves of the same query
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    // lanes l and l + 32 hold the two key quarters of the same query
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    // the running max is raised only when a score passes it by more than
-    // kLazyMax, so O is rarely rescaled; weights stay below 2^kLazyMax
     const float mt = mx * scale_log2;
     const bool moved = mt > w.m + kLazyMax;
     const float m_new = moved ? mt : w.m;
@@ -164,43 +153,103 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
     w.m = m_new;
     float rs = 0.f;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(fmaf(s[sub][i], scale_log2, -m_new));
-            s[sub][i] = p;
-            rs += p;
-        }
+    for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[i], scale_log2, -m_new));
+        s[i] = p;
+        rs += p;
+    }
     w.l = w.l * alpha + rs;
     // rescale O only when some running max of the wave was raised
     if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
         for (int dt = 0; dt < Wave<D>::DT; ++dt) w.o[dt] *= alpha;
     }
+}
 
+// Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
+// O^T += V^T P^T over one 32-key half of the tile. The V^T operands are read
+// two MFMAs ahead of their use, so the LDS latency hides behind the matrix
+// work.
+template <int D>
+HSAKV_DEV void pv_half(Wave<D>& w, const f32x16_t& s, const char* vt, int sub) {
+    using LY = Lay<D>;
+    constexpr int DT = Wave<D>::DT;
+    const int lane = threadIdx.x & 63;
     const int G = lane >> 4, j = lane & 15;
+    bf16x8_t pf[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            bf16x8_t pf;
+        for (int e = 0; e < 8; ++e) pf[c][e] = (__bf16)s[8 * c + e];
+    i16x4_t lo[2][DT], hi[2][DT];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[sub][8 * c + e];
-            const int krow = 32 * sub + 16 * c + 4 * (G >> 1) + (j >> 2);
+    for (int c = 0; c < 2; ++c) {
+        const int krow = 32 * sub + 16 * c + 4 * (G >> 1) + (j >> 2);
 #pragma unroll
-            for (int dt = 0; dt < Wave<D>::DT; ++dt) {
-                const int dcol = 32 * dt + 16 * (G & 1) + 4 * (j & 3);
-                const int lo_off = krow * LY::ROWB + (((dcol >> 3) ^ LY::swz_v(krow)) << 4) + ((dcol & 7) << 1);
-                const int hi_off = (krow + 8) * LY::ROWB + (((dcol >> 3) ^ LY::swz_v(krow + 8)) << 4) +
-                                   ((dcol & 7) << 1);
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + lo_off));
-                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + hi_off));
-                const i16x8_t vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                w.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf,
-                                                                  w.o[dt], 0, 0, 0);
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            const int dcol = 32 * dt + 16 * (G & 1) + 4 * (j & 3);
+            const int lo_off = krow * LY::ROWB + (((dcol >> 3) ^ LY::swz_v(krow)) << 4) + ((dcol & 7) << 1);
+            const int hi_off = (krow + 8) * LY::ROWB + (((dcol >> 3) ^ LY::swz_v(krow + 8)) << 4) +
+                               ((dcol & 7) << 1);
+            lo[c][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + lo_off));
+            hi[c][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + hi_off));
         }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const i16x8_t vv = __builtin_shufflevector(lo[c][dt], hi[c][dt], 0, 1, 2, 3, 4, 5, 6, 7);
+            w.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[c], w.o[dt], 0, 0, 0);
+        }
+    // 4 reads ahead, then one MFMA per two reads, then the last two MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 2 * DT - 2; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+}
+
+// One 64-key tile as two 32-key online-softmax steps. The order S(0), S(1),
+// softmax(0), PV(0), softmax(1), PV(1) lets the matrix cores run S(1) and
+// PV(0) while the vector ALUs work on the softmax of the other half.
+template <int D>
+HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid, float scale_log2) {
+    using LY = Lay<D>;
+    const int lane = threadIdx.x & 63;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    constexpr int KS = Wave<D>::KS;
+    // K operands read four MFMAs ahead of their use
+    bf16x8_t a[2][KS];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int row = 32 * sub + r32;
+            a[sub][ks] = *reinterpret_cast<const bf16x8_t*>(kt + row * LY::ROWB + (((2 * ks + g2) ^ LY::swz_k(row)) << 4));
+        }
+    f32x16_t s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[sub][ks], w.qf[ks], s[sub], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 2 * KS - 4; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    softmax_half<D>(w, s[0], 0, nvalid, scale_log2);
+    pv_half<D>(w, s[0], vt, 0);
+    softmax_half<D>(w, s[1], 1, nvalid, scale_log2);
+    pv_half<D>(w, s[1], vt, 1);
 }
 
 // Key block b -> token range and source (history blocks first, then chunk blocks).
