@@ -52,6 +52,7 @@ constexpr int kSparseMaxWg = 256; // attention work-groups at most (partials are
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -60,7 +61,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // lane l at base + 16 l. Rows are D bf16 (no padding); the 16-byte slots of
 // row r are XOR-swizzled so the MFMA operand reads hit distinct banks:
 //   K: slot s of row r holds chunk s ^ (r mod CPR)        (16 rows, one chunk)
-//   V: slot s of row r holds chunk s ^ (2r mod CPR)       (4 rows, two chunks)
+//   V: slot s of row r holds chunk s ^ 4 (r mod 4) for D = 128 (a transpose
+//      read's 4 rows x 4 chunks per 32 lanes on 16 distinct slots), else
+//      chunk s ^ (2r mod CPR)
 template <int D>
 struct Lay {
     static constexpr int ROWB = D * 2;                    // bytes per key row
@@ -72,7 +75,7 @@ struct Lay {
     static constexpr int VM_PER_TILE = 2 * PER_WAVE;      // vector-memory ops per wave and tile
     static_assert(INSTR % NW == 0, "DMA instructions split evenly over the waves");
     HSAKV_DEV static int swz_k(int r) { return r & (CPR - 1); }
-    HSAKV_DEV static int swz_v(int r) { return (2 * r) & (CPR - 1); }
+    HSAKV_DEV static int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : (2 * r) & (CPR - 1); }
 };
 
 // DMA one tile (64 key rows of K and V) into an LDS buffer. Rows past `nvalid`
@@ -151,14 +154,10 @@ HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float 
     const float m_new = moved ? mt : w.m;
     const float alpha = moved ? fast_exp2(w.m - m_new) : 1.0f;
     w.m = m_new;
-    float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[i], scale_log2, -m_new));
-        s[i] = p;
-        rs += p;
-    }
-    w.l = w.l * alpha + rs;
+    for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_new));
+    // the half's weights are added to the row sum by pv_half, as rounded for the MFMA
+    w.l *= alpha;
     // rescale O only when some running max of the wave was raised
     if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
@@ -169,9 +168,10 @@ HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float 
 // Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
-// O^T += V^T P^T over one 32-key half of the tile. The V^T operands are read
-// two MFMAs ahead of their use, so the LDS latency hides behind the matrix
-// work.
+// O^T += V^T P^T over one 32-key half of the tile, and the half's weights
+// (bf16, as the MFMA takes them) added to this lane's share of the row sum by
+// dot products with ones. The V^T operands are read two MFMAs ahead of their
+// use, so the LDS latency hides behind the matrix work.
 template <int D>
 HSAKV_DEV void pv_half(Wave<D>& w, const f32x16_t& s, const char* vt, int sub) {
     using LY = Lay<D>;
@@ -183,6 +183,14 @@ HSAKV_DEV void pv_half(Wave<D>& w, const f32x16_t& s, const char* vt, int sub) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[c][e] = (__bf16)s[8 * c + e];
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs = w.l;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[c][2 * e], pf[c][2 * e + 1]}, ones, rs, false);
+    w.l = rs;
     i16x4_t lo[2][DT], hi[2][DT];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -658,7 +666,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     const int total = a1 - a0;
     if (total <= 0) return;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int myr = wave >> 1;
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
