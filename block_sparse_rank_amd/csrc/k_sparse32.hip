@@ -46,6 +46,7 @@ namespace {
 constexpr int KT = 64;            // keys per tile
 constexpr int R = 4;              // rows (query blocks) per group
 constexpr int NW = 2 * R;         // waves per work-group, 32 queries each
+static_assert(R <= 8, "a tile descriptor holds the row mask in bits 7..14");
 constexpr float kLazyMax = 8.0f;  // margin (log2 units) before the running max is raised
 constexpr int kPlanThreads = 256;
 constexpr int kSparseMaxWg = 256; // attention work-groups at most (partials are sized for it)
@@ -78,6 +79,39 @@ struct Lay {
     HSAKV_DEV static int swz_v(int r) { return CPR == 16 ? 4 * (r & 3) : (2 * r) & (CPR - 1); }
 };
 
+// This wave's DMA lanes, fixed over the tiles: instruction j covers slots
+// (wave PER_WAVE + j) 64 + lane, i.e. key row r and, after the swizzle, the
+// 16-byte chunk ck (K) / cv (V) of that row (byte offsets within the row).
+template <int D>
+struct DmaLanes {
+    int r[Lay<D>::PER_WAVE], ck[Lay<D>::PER_WAVE], cv[Lay<D>::PER_WAVE];
+};
+
+template <int D>
+HSAKV_DEV void dma_lanes(DmaLanes<D>& dl, int wave) {
+    using LY = Lay<D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < LY::PER_WAVE; ++j) {
+        const int L = (wave * LY::PER_WAVE + j) * 64 + lane;
+        const int r = L / LY::CPR, sl = L % LY::CPR;
+        dl.r[j] = r;
+        dl.ck[j] = (sl ^ LY::swz_k(r)) << 4;
+        dl.cv[j] = (sl ^ LY::swz_v(r)) << 4;
+    }
+}
+
+// The LDS destination of a tile DMA as an address the compiler cannot trace
+// back to the ring buffer it lands in. The kernel orders every DMA before the
+// reads of its buffer itself (a vmcnt wait on the tiles sent, then the
+// work-group barrier); the compiler's own tracking of LDS DMA targets, which
+// merges the paths of a partly filled ring, would add waits that drain the
+// tiles in flight too.
+HSAKV_DEV lds_void_t* dma_dst(char* p) {
+    const uint32_t v = (uint32_t)(uintptr_t)(lds_void_t*)p;
+    return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
+}
+
 // DMA one tile (64 key rows of K and V) into an LDS buffer. Rows past `nvalid`
 // (the ragged end of a block) load the last valid row: their scores are
 // masked to -inf, so P = 0 multiplies finite values. The DMA goes through
@@ -86,21 +120,18 @@ struct Lay {
 // exact lgkmcnt waits and can be issued ahead of their MFMAs (a pending
 // global_load_lds makes every LDS read wait for all earlier ones).
 template <int D>
-HSAKV_DEV void dma_tile(char* buf, const bf16_t* kb, const bf16_t* vb, int nvalid, int HD) {
+HSAKV_DEV void dma_tile(char* buf, const bf16_t* kb, const bf16_t* vb, int nvalid, int row_bytes,
+                        const DmaLanes<D>& dl, int wave) {
     using LY = Lay<D>;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kb), 0, -1, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vb), 0, -1, 0x00020000);
 #pragma unroll
     for (int j = 0; j < LY::PER_WAVE; ++j) {
         const int slot0 = (wave * LY::PER_WAVE + j) * 64;
-        const int L = slot0 + lane;
-        const int r = L / LY::CPR, sl = L % LY::CPR;
-        const int rg = r < nvalid ? r : nvalid - 1;
-        const int offk = rg * HD + ((sl ^ LY::swz_k(r)) << 3);
-        const int offv = rg * HD + ((sl ^ LY::swz_v(r)) << 3);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(buf + slot0 * 16), 16, 2 * offk, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(buf + LY::MAT + slot0 * 16), 16, 2 * offv, 0, 0, 0);
+        const int rg = dl.r[j] < nvalid ? dl.r[j] : nvalid - 1;
+        const int ro = (int)__umul24((unsigned)rg, (unsigned)row_bytes);   // rg < 64, row_bytes < 2^24
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dma_dst(buf + slot0 * 16), 16, ro + dl.ck[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dma_dst(buf + LY::MAT + slot0 * 16), 16, ro + dl.cv[j], 0, 0, 0);
     }
 }
 
@@ -489,12 +520,14 @@ k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restri
     }
 }
 
-// Union of the selected blocks of one group's rows, in ascending block order:
-// uni[e] = block | row_mask << 16 and upre[e] = tiles of the entries before e.
+// Union of the selected blocks of one group's rows, in ascending block order,
+// as one descriptor per 64-key tile: tdesc[grp * tpg + t] = (first token row
+// of the tile in its source, valid keys | row mask << 7 | 1 << 15 for a
+// history tile).
 __global__ void __launch_bounds__(kPlanThreads)
 k_plan_groups(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
-              const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ grows, int32_t* __restrict__ uni,
-              int32_t* __restrict__ upre, int32_t* __restrict__ gcount, int32_t* __restrict__ gtiles) {
+              const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ grows, int2* __restrict__ tdesc,
+              int tpg, int32_t* __restrict__ gcount, int32_t* __restrict__ gtiles) {
     __shared__ int mask[4096];
     __shared__ int wsum[2][kPlanThreads / 64];
     const int grp = blockIdx.x, tid = threadIdx.x;
@@ -528,17 +561,17 @@ k_plan_groups(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restr
             nt += (open_block(g, NBh, Lh, b).len + KT - 1) / KT;
         }
     int ce_tot, ct_tot;
-    int ce = block_excl_scan<kPlanThreads>(ne, &ce_tot, wsum[0]);
+    block_excl_scan<kPlanThreads>(ne, &ce_tot, wsum[0]);
     int ct = block_excl_scan<kPlanThreads>(nt, &ct_tot, wsum[1]);
-    int32_t* u = uni + (size_t)grp * g.NB_max;
-    int32_t* p = upre + (size_t)grp * g.NB_max;
+    int2* td = tdesc + (size_t)grp * tpg;
     for (int b = b0; b < b1; ++b) {
         const int mk = mask[b];
         if (mk) {
-            u[ce] = b | (mk << 16);
-            p[ce] = ct;
-            ++ce;
-            ct += (open_block(g, NBh, Lh, b).len + KT - 1) / KT;
+            const Cursor c = open_block(g, NBh, Lh, b);
+            for (int t = 0; t * KT < c.len; ++t) {
+                const int nvalid = c.len - t * KT < KT ? c.len - t * KT : KT;
+                td[ct++] = int2{(int)(c.t0 + (long long)t * KT), nvalid | (mk << 7) | (c.hist ? 1 << 15 : 0)};
+            }
         }
     }
     if (tid == 0) {
@@ -648,7 +681,7 @@ __global__ void __launch_bounds__(64 * NW)
 k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_hist,
                 const bf16_t* __restrict__ v_hist, const bf16_t* __restrict__ k_intra,
                 const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
-                const int32_t* __restrict__ uni, const int32_t* __restrict__ upre,
+                const int2* __restrict__ tdesc, int tpg,
                 const int32_t* __restrict__ gcount, const int32_t* __restrict__ gtiles,
                 const int32_t* __restrict__ gstart, PlanArgs pl, int per_xcd, Epi ep) {
     using LY = Lay<D>;
@@ -668,11 +701,10 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int myr = wave >> 1;
-    const int n_sel = *n_sel_p;
-    const int NBh = hist_blocks(g, n_sel);
-    const long long Lh = (long long)n_sel * g.Tp;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     const int gph = groups_per_head(g);
+    DmaLanes<D> dl;
+    dma_lanes<D>(dl, wave);
 
     // The range holds pieces of consecutive groups: the tail of the first
     // (its highest blocks) when the range starts inside it, whole groups, and
@@ -690,28 +722,6 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         return p;
     };
     int pg = wrap ? next_group(g0) : g0;
-    int pe, pt, pmask, pntile;
-    Cursor pc;
-    auto load_entry = [&]() __attribute__((always_inline)) {
-        const int v = uni[(size_t)pg * g.NB_max + pe];
-        pmask = v >> 16;
-        pc = open_block(g, NBh, Lh, v & 0xffff);
-        pntile = (pc.len + KT - 1) / KT;
-    };
-    // producer position: the tile `lo` (global sequence) of group pg
-    auto seek = [&](int lo) __attribute__((always_inline)) {
-        pe = last_le(upre + (size_t)pg * g.NB_max, gcount[pg], lo - gstart[pg]);
-        pt = lo - gstart[pg] - upre[(size_t)pg * g.NB_max + pe];
-        load_entry();
-    };
-    // next tile of the same group (the caller knows one exists)
-    auto advance = [&]() __attribute__((always_inline)) {
-        if (++pt >= pntile) {
-            pt = 0;
-            ++pe;
-            load_entry();
-        }
-    };
 
     Wave<D> w;
     int done = 0;     // tiles of the range computed
@@ -722,8 +732,11 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         const int h = grp / gph, i = pl.grows[grp * R + myr];
         const int S = gstart[grp], Tg = gtiles[grp];
         const int lo = S > a0 ? S : a0, hi = S + Tg < a1 ? S + Tg : a1;
-        seek(lo);
         const int end = hi - lo;
+        // the piece's tile descriptors; the next one to send is loaded at the
+        // end of the step before, so its latency hides under that step's MFMAs
+        const int2* td = tdesc + (size_t)grp * tpg + (lo - S);
+        int2 dnext = td[0];
         int n = 0;        // tiles of the piece computed
         int issued = 0;   // tiles of the piece sent
         const long long hoff = (long long)h * D;
@@ -731,18 +744,24 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         // tile info for the consumer: row mask << 7 | valid keys
         int info0 = 0, info1 = 0, info2 = 0, info3 = 0;
         auto issue = [&](char* dst) __attribute__((always_inline)) -> int {
-            const int nvalid = pc.len - pt * KT < KT ? pc.len - pt * KT : KT;
-            const long long t0 = pc.t0 + (long long)pt * KT;
-            const bf16_t* kb = (pc.hist ? k_hist : k_intra) + hoff + t0 * g.HD;
-            const bf16_t* vb = (pc.hist ? v_hist : v_intra) + hoff + t0 * g.HD;
-            dma_tile<D>(dst, kb, vb, nvalid, g.HD);
-            const int inf = (pmask << 7) | nvalid;
-            if (++issued < end) advance();
-            return inf;
+            const int2 d = dnext;
+            ++issued;
+            const long long roff = hoff + (long long)d.x * g.HD;
+            const bool hist = (d.y >> 15) & 1;
+            dma_tile<D>(dst, (hist ? k_hist : k_intra) + roff, (hist ? v_hist : v_intra) + roff, d.y & 127,
+                        2 * g.HD, dl, wave);
+            return d.y & 0x7fff;   // row mask << 7 | valid keys
         };
         info0 = issue(lds0);
-        if (issued < end) info1 = issue(lds1);
-        if (issued < end) info2 = issue(lds2);
+        if (issued < end) {
+            dnext = td[issued];
+            info1 = issue(lds1);
+        }
+        if (issued < end) {
+            dnext = td[issued];
+            info2 = issue(lds2);
+        }
+        if (issued < end) dnext = td[issued];
         auto step = [&](const char* now, char* nxt, int inf, int& inf_nxt) __attribute__((always_inline)) {
             // this wave's DMA of tile n has landed once at most the tiles sent
             // after it are outstanding; the barrier makes every wave's part
@@ -757,6 +776,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
             lds_barrier();
             if (issued < end) inf_nxt = issue(nxt);
             if ((inf >> (7 + myr)) & 1) tile_step<D>(w, now, now + LY::MAT, inf & 127, scale_log2);
+            if (issued < end) dnext = td[issued];
         };
         while (true) {
             step(lds0, lds3, info0, info3);
@@ -860,12 +880,18 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SparseWs {
     uint32_t* tbits;
-    int32_t *grows, *uni, *upre, *gcount, *gtiles, *gstart;
+    int32_t* grows;
+    int2* tdesc;
+    int32_t *gcount, *gtiles, *gstart;
     float* part_o;
     float2* part_ml;
 };
 
 int n_groups(const Geo& g) { return g.H * ((g.NQB + R - 1) / R); }
+// Tiles of a group's union at most (every block of the head selected).
+int tiles_per_group(const Geo& g) {
+    return ((g.Binter + KT - 1) / KT) * g.NBh_max + ((g.Bintra + KT - 1) / KT) * g.NBc;
+}
 size_t part_o_bytes(const Geo& g) { return al256((size_t)kSparseMaxWg * 2 * NW * 64 * 16 * 4 * (g.d / 32)); }
 size_t part_ml_bytes() { return al256((size_t)kSparseMaxWg * 2 * NW * 64 * 8); }
 
@@ -875,8 +901,7 @@ SparseWs carve(const Geo& g, void* ws) {
     SparseWs s;
     s.tbits = (uint32_t*)p;  p += al256((size_t)g.H * g.NQB * kGroupWords * 4);
     s.grows = (int32_t*)p;   p += al256((size_t)NG * R * 4);
-    s.uni = (int32_t*)p;     p += al256((size_t)NG * g.NB_max * 4);
-    s.upre = (int32_t*)p;    p += al256((size_t)NG * g.NB_max * 4);
+    s.tdesc = (int2*)p;      p += al256((size_t)NG * tiles_per_group(g) * 8);
     s.gcount = (int32_t*)p;  p += al256((size_t)NG * 4);
     s.gtiles = (int32_t*)p;  p += al256((size_t)NG * 4);
     s.gstart = (int32_t*)p;  p += al256((size_t)(NG + 1) * 4);
@@ -890,7 +915,7 @@ SparseWs carve(const Geo& g, void* ws) {
 size_t sparse_bf16_ws_bytes(const Geo& g) {
     const int NG = n_groups(g);
     return al256((size_t)g.H * g.NQB * kGroupWords * 4) + al256((size_t)NG * R * 4) +
-           2 * al256((size_t)NG * g.NB_max * 4) + 2 * al256((size_t)NG * 4) +
+           al256((size_t)NG * tiles_per_group(g) * 8) + 2 * al256((size_t)NG * 4) +
            al256((size_t)(NG + 1) * 4) + part_o_bytes(g) + part_ml_bytes();
 }
 
@@ -904,7 +929,7 @@ void launch_sparse_plan_bf16(const Geo& g, const int32_t* n_sel, const int32_t* 
     hipLaunchKernelGGL(k_plan_rows, dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel, (const uint32_t*)s.tbits,
                        s.grows);
     hipLaunchKernelGGL(k_plan_groups, dim3(NG), dim3(kPlanThreads), 0, st, g, n_sel, sel_count, sel_idx,
-                       (const int32_t*)s.grows, s.uni, s.upre, s.gcount, s.gtiles);
+                       (const int32_t*)s.grows, s.tdesc, tiles_per_group(g), s.gcount, s.gtiles);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, NG, (const int32_t*)s.gtiles, s.gstart);
 }
 
@@ -919,7 +944,7 @@ void launch_compute_d(const Geo& g, const void* q, const void* k_hist, const voi
     const int per_xcd = (pl.G + 7) / 8;
     hipLaunchKernelGGL((k_sparse_attn32<D>), dim3(8 * per_xcd), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
                        (const bf16_t*)k_hist, (const bf16_t*)v_hist, (const bf16_t*)k_intra,
-                       (const bf16_t*)v_intra, n_sel, (const int32_t*)s.uni, (const int32_t*)s.upre,
+                       (const bf16_t*)v_intra, n_sel, (const int2*)s.tdesc, tiles_per_group(g),
                        (const int32_t*)s.gcount, (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl,
                        per_xcd, ep);
     hipLaunchKernelGGL((k_sparse_combine<D>), dim3(NG), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
