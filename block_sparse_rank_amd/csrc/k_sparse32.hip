@@ -101,15 +101,14 @@ HSAKV_DEV void dma_lanes(DmaLanes<D>& dl, int wave) {
     }
 }
 
-// The LDS destination of a tile DMA as an address the compiler cannot trace
-// back to the ring buffer it lands in. The kernel orders every DMA before the
+// The LDS byte address of a ring buffer as a value the compiler cannot trace
+// back to the buffer, for the tile DMA. The kernel orders every DMA before the
 // reads of its buffer itself (a vmcnt wait on the tiles sent, then the
 // work-group barrier); the compiler's own tracking of LDS DMA targets, which
 // merges the paths of a partly filled ring, would add waits that drain the
 // tiles in flight too.
-HSAKV_DEV lds_void_t* dma_dst(char* p) {
-    const uint32_t v = (uint32_t)(uintptr_t)(lds_void_t*)p;
-    return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
+HSAKV_DEV uint32_t dma_base(char* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)p);
 }
 
 // DMA one tile (64 key rows of K and V) into an LDS buffer. Rows past `nvalid`
@@ -120,7 +119,7 @@ HSAKV_DEV lds_void_t* dma_dst(char* p) {
 // exact lgkmcnt waits and can be issued ahead of their MFMAs (a pending
 // global_load_lds makes every LDS read wait for all earlier ones).
 template <int D>
-HSAKV_DEV void dma_tile(char* buf, const bf16_t* kb, const bf16_t* vb, int nvalid, int row_bytes,
+HSAKV_DEV void dma_tile(uint32_t buf, const bf16_t* kb, const bf16_t* vb, int nvalid, int row_bytes,
                         const DmaLanes<D>& dl, int wave) {
     using LY = Lay<D>;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kb), 0, -1, 0x00020000);
@@ -130,8 +129,9 @@ HSAKV_DEV void dma_tile(char* buf, const bf16_t* kb, const bf16_t* vb, int nvali
         const int slot0 = (wave * LY::PER_WAVE + j) * 64;
         const int rg = dl.r[j] < nvalid ? dl.r[j] : nvalid - 1;
         const int ro = (int)__umul24((unsigned)rg, (unsigned)row_bytes);   // rg < 64, row_bytes < 2^24
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dma_dst(buf + slot0 * 16), 16, ro + dl.ck[j], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dma_dst(buf + LY::MAT + slot0 * 16), 16, ro + dl.cv[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(uintptr_t)(buf + slot0 * 16), 16, ro + dl.ck[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(uintptr_t)(buf + LY::MAT + slot0 * 16), 16,
+                                                 ro + dl.cv[j], 0, 0, 0);
     }
 }
 
@@ -166,11 +166,10 @@ template <int D>
 HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float scale_log2) {
     const int g2 = (threadIdx.x & 63) >> 5;
     if (nvalid < 32 * (sub + 1)) {
+        // element i holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4: valid below t
+        const int t = nvalid - 32 * sub - 4 * g2;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = 32 * sub + 8 * (i >> 2) + 4 * g2 + (i & 3);
-            if (key >= nvalid) s[i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < t ? s[i] : -INFINITY;
     }
     // raw scores: the max is taken before scaling (scale > 0), and the scale
     // folds into the exponent's FMA
@@ -705,6 +704,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     const int gph = groups_per_head(g);
     DmaLanes<D> dl;
     dma_lanes<D>(dl, wave);
+    const uint32_t b0 = dma_base(lds0), b1 = dma_base(lds1), b2 = dma_base(lds2), b3 = dma_base(lds3);
 
     // The range holds pieces of consecutive groups: the tail of the first
     // (its highest blocks) when the range starts inside it, whole groups, and
@@ -743,7 +743,7 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         start_rows<D>(g, q, h, i, w);
         // tile info for the consumer: row mask << 7 | valid keys
         int info0 = 0, info1 = 0, info2 = 0, info3 = 0;
-        auto issue = [&](char* dst) __attribute__((always_inline)) -> int {
+        auto issue = [&](uint32_t dst) __attribute__((always_inline)) -> int {
             const int2 d = dnext;
             ++issued;
             const long long roff = hoff + (long long)d.x * g.HD;
@@ -752,17 +752,17 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
                         2 * g.HD, dl, wave);
             return d.y & 0x7fff;   // row mask << 7 | valid keys
         };
-        info0 = issue(lds0);
+        info0 = issue(b0);
         if (issued < end) {
             dnext = td[issued];
-            info1 = issue(lds1);
+            info1 = issue(b1);
         }
         if (issued < end) {
             dnext = td[issued];
-            info2 = issue(lds2);
+            info2 = issue(b2);
         }
         if (issued < end) dnext = td[issued];
-        auto step = [&](const char* now, char* nxt, int inf, int& inf_nxt) __attribute__((always_inline)) {
+        auto step = [&](const char* now, uint32_t nxt, int inf, int& inf_nxt) __attribute__((always_inline)) {
             // this wave's DMA of tile n has landed once at most the tiles sent
             // after it are outstanding; the barrier makes every wave's part
             // visible and retires every read of `nxt` (tile n - 1)
@@ -779,13 +779,13 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
             if (issued < end) dnext = td[issued];
         };
         while (true) {
-            step(lds0, lds3, info0, info3);
+            step(lds0, b3, info0, info3);
             if (++n == end) break;
-            step(lds1, lds0, info1, info0);
+            step(lds1, b0, info1, info0);
             if (++n == end) break;
-            step(lds2, lds1, info2, info1);
+            step(lds2, b1, info2, info1);
             if (++n == end) break;
-            step(lds3, lds2, info3, info2);
+            step(lds3, b2, info3, info2);
             if (++n == end) break;
         }
         if (S >= a0 && S + Tg <= a1) {
