@@ -220,8 +220,8 @@ def stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops, ga
     traffic = recorded_traffic("hsa_sparse_attn", s.name)
     return {
         "stages_ms": {k: round(v, 4) for k, v in ms.items()},
-        "roofline": {"kernel": "hsa_sparse_attn (k_plan_groups, k_plan_scan, k_sparse_attn32, "
-                               "k_sparse_combine)",
+        "roofline": {"kernel": "hsa_sparse_attn (k_plan_bits, k_plan_rows, k_plan_groups, k_plan_scan, "
+                               "k_sparse_attn32, k_sparse_combine)",
                      "bound": "mfma", "achieved": round(att_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(att_tflops / peak, 4),
                      "traffic": traffic, "algorithmic_flops": sparse_flops},

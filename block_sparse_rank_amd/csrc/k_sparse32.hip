@@ -9,8 +9,8 @@
 // is four rows of one head, chosen by a plan kernel so that their selections
 // overlap (greedy, see k_plan_rows), and its work is the union of the four
 // rows' selected blocks, cut into 64-key tiles. A plan kernel writes each group's
-// union in ascending block order with the tile offset of every entry, and the
-// group tile totals are scanned into one global tile sequence. The attention
+// union in ascending block order as one descriptor per tile, and the group
+// tile totals are scanned into one global tile sequence. The attention
 // kernel then gives work-group k the tiles [kT/G, (k+1)T/G) of that sequence
 // (T tiles, G work-groups, one per CU), so every CU gets the same number of
 // tiles whatever the rows' selection sizes. A group whose tiles are split
@@ -37,7 +37,9 @@
 // tile is covered by three tiles of MFMA work and no registers hold data in
 // flight. Work-group b runs on XCD b % 8 and takes range (b % 8) * G/8 + b / 8,
 // so neighbouring ranges (groups of one head, which select many of the same
-// blocks) share an XCD's L2.
+// blocks) share an XCD's L2; within a range the tiles are taken in ascending
+// block order (see the attention kernel), so those ranges also read nearby
+// blocks at the same time.
 #include "common.h"
 #include "launch.h"
 
