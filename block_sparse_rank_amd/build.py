@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhsakv.so")
 
-SOURCES = ["api.hip", "k_hkv.hip", "k_select.hip", "k_attn.hip", "k_sparse32.hip", "k_linear.hip", "k_proj32.hip"]
+SOURCES = ["api.hip", "k_hkv.hip", "k_select.hip", "k_attn.hip", "k_sparse32.hip", "k_linear.hip", "k_proj32.hip", "k_lowrank32.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

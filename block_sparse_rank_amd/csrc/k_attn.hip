@@ -429,6 +429,11 @@ template void launch_sparse_attn<bf16_t>(const Geo&, const void*, const void*, c
 template <typename T>
 void launch_lowrank_attn(const Geo& g, const void* q, const void* k_hi, const void* v_hi,
                          const void* k_lo, const void* v_lo, const Epi& ep, hipStream_t st) {
+    if (sizeof(T) == 2 && !ep.out && ep.o_main && (g.d == 64 || g.d == 128)) {
+        // bf16: the 32x32x16 MFMA kernel (k_lowrank32.hip)
+        launch_lowrank_attn_bf16_mfma32(g, q, k_hi, v_hi, k_lo, v_lo, ep.o_main, st);
+        return;
+    }
     dim3 grid(g.H * g.NQB);
     constexpr bool LO = sizeof(T) == 2;
     if (g.d == 128)

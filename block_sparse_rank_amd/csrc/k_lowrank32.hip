@@ -1,0 +1,284 @@
+// Low-rank branch attention, bf16, on gfx950 32x32x16 MFMA.
+//
+// Pages: WorldAttention news summary (ai4snews), HSA paragraph (a
+// Linformer-style low-rank global branch, O(L r)); the projection is the
+// Linformer paper's (cited on the mlsanity map). Every query attends, with
+// exact softmax, to the r projected keys K' = E K_act with the projected
+// values V' = F V_act of its head.
+//
+// K' and V' come as bf16 hi + lo pairs (hi = bf16(x), lo = bf16(x - hi)), so
+// a product with them keeps about 16 mantissa bits:
+//   S^T = K'_hi Q^T + K'_lo Q^T,   O^T += V'_hi^T P^T + V'_lo^T P^T.
+//
+// Work-group = 8 waves, 32 queries each: 256 consecutive queries of one head.
+// The r keys stream through LDS in 64-key tiles (K'_hi, K'_lo, V'_hi, V'_lo),
+// two buffers, the next tile's DMA in flight while the current one is
+// computed. Rows are padded for conflict-free operand reads with plain base +
+// immediate addresses: a K row holds its D/8 16-byte chunks and one pad slot,
+// a V row its chunks and four pad slots (a DMA pad lane loads the row's first
+// chunk again, into the pad). The DMA uses buffer loads whose resource ends at
+// the tile's last valid key row, so rows past r read as zero; their scores
+// are masked to -inf before the softmax.
+//
+// In the 32x32 accumulator layout lane l holds query l%32 and keys
+// 8a + 4(l/32) + b (a, b = 0..3) of a 32-key half. A 16-key chunk c of those
+// registers is the P^T operand with k order
+//   e < 4: key 16c + 4(l/32) + e,   e >= 4: key 16c + 8 + 4(l/32) + e - 4
+// and the V^T operand comes in the same key order from ds_read_b64_tr_b16
+// transpose reads of the row-major V tile, so P never leaves its lane. Each
+// half is one online-softmax step (float32, exp2 with the log2(e)/sqrt(d)
+// scale folded into the exponent's FMA); the row sum is taken on the bf16
+// weights the MFMA consumes.
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int LT = 64;        // keys per tile
+constexpr int LW = 8;         // waves per work-group
+constexpr int LQ = 32 * LW;   // queries per work-group
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int D>
+struct LLay {
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int KSL = CPR + 1, VSL = CPR + 4;    // LDS slots per K / V row
+    static constexpr int KP = 16 * KSL, VP = 16 * VSL;    // LDS row pitches (bytes)
+    static constexpr int KMAT = LT * KP, VMAT = LT * VP;
+    // buffer: K'_hi, K'_lo, V'_hi, V'_lo
+    static constexpr int KLO = KMAT, VHI = 2 * KMAT, VLO = 2 * KMAT + VMAT, BUF = 2 * KMAT + 2 * VMAT;
+    static constexpr int NI = 2 * KSL + 2 * VSL;          // DMA instructions per tile (64 rows each)
+    static constexpr int PER_WAVE = (NI + LW - 1) / LW;   // per wave, the last ones idle
+    static constexpr int KS = D / 16, DT = D / 32;
+};
+
+template <int D>
+struct LWave {
+    bf16x8_t qf[LLay<D>::KS];
+    f32x16_t o[LLay<D>::DT];
+    float m, l;   // running max (log2 units), this lane's share of the row sum
+};
+
+// This wave's DMA instructions j = wave + LW q: matrix mat (0 K'_hi, 1 K'_lo,
+// 2 V'_hi, 3 V'_lo, 4 idle), LDS offset of the instruction within the buffer,
+// and per lane the source byte offset within the tile (row r, chunk c).
+template <int D>
+struct LDma {
+    int off[LLay<D>::PER_WAVE];
+};
+
+template <int D>
+HSAKV_DEV int dma_mat(int j) {
+    using LY = LLay<D>;
+    return j < LY::KSL ? 0 : j < 2 * LY::KSL ? 1 : j < 2 * LY::KSL + LY::VSL ? 2 : j < LY::NI ? 3 : 4;
+}
+
+template <int D>
+HSAKV_DEV void ldma_lanes(LDma<D>& dl, int wave, int row_bytes) {
+    using LY = LLay<D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < LY::PER_WAVE; ++q) {
+        const int j = wave + LW * q;
+        const int mat = dma_mat<D>(j);
+        const int j0 = mat == 0 ? 0 : mat == 1 ? LY::KSL : mat == 2 ? 2 * LY::KSL : 2 * LY::KSL + LY::VSL;
+        const int sl_n = mat < 2 ? LY::KSL : LY::VSL;
+        const int L = (j - j0) * 64 + lane;
+        const int r = L / sl_n, sl = L % sl_n;
+        dl.off[q] = mat < 4 ? r * row_bytes + (sl < LY::CPR ? 16 * sl : 0) : 0;
+    }
+}
+
+HSAKV_DEV uint32_t lds_addr(char* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)p);
+}
+
+// DMA the tile of keys [t0, t0 + nvalid) into the buffer at LDS address buf.
+// Each source resource ends at the tile's last valid row, so rows past it are
+// out of range and land as zeros; idle instructions have an empty resource
+// and land in `spare`.
+template <int D>
+HSAKV_DEV void ldma_tile(uint32_t buf, uint32_t spare, const bf16_t* const (&src)[4], long long t0, int nvalid,
+                         int HD, const LDma<D>& dl, int wave) {
+    using LY = LLay<D>;
+    const int bytes = ((nvalid - 1) * HD + D) * 2;
+    __amdgpu_buffer_rsrc_t rs[5];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        rs[m] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(src[m] + t0 * HD), 0, bytes, 0x00020000);
+    rs[4] = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(src[0]), 0, 0, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < LY::PER_WAVE; ++q) {
+        const int j = wave + LW * q;
+        const int mat = dma_mat<D>(j);
+        const uint32_t dst = mat < 4 ? buf + 1024u * j : spare;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[mat], (lds_void_t*)(uintptr_t)dst, 16, dl.off[q], 0, 0, 0);
+    }
+}
+
+template <int N>
+HSAKV_DEV void lwait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+HSAKV_DEV void llds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One 32-key half: masking past nvalid, online softmax, O^T += V^T P^T for
+// both V parts.
+template <int D>
+HSAKV_DEV void lhalf(LWave<D>& w, f32x16_t& s, const char* buf, int sub, int nvalid, float scale_log2) {
+    using LY = LLay<D>;
+    const int lane = threadIdx.x & 63;
+    const int g2 = lane >> 5, G = lane >> 4, j = lane & 15;
+    if (nvalid < 32 * (sub + 1)) {
+        const int t = nvalid - 32 * sub - 4 * g2;   // element i holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < t ? s[i] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    // a half of a tile can hold no valid key at all (mx = -inf): no change then
+    const float mt = mx * scale_log2;
+    const float m_new = fmaxf(w.m, mt);
+    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(w.m - m_new);
+    w.m = m_new;
+    bf16x8_t pf[2];
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs = w.l * alpha;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pf[c][e] = (__bf16)(m_new == -INFINITY ? 0.f : fast_exp2(fmaf(s[8 * c + e], scale_log2, -m_new)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[c][2 * e], pf[c][2 * e + 1]}, ones, rs, false);
+    }
+    w.l = rs;
+#pragma unroll
+    for (int dt = 0; dt < LY::DT; ++dt) w.o[dt] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int krow = 32 * sub + 16 * c + 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+        for (int dt = 0; dt < LY::DT; ++dt) {
+            const int off = krow * LY::VP + 2 * (32 * dt + 16 * (G & 1) + 4 * (j & 3));
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                const char* vt = buf + (part ? LY::VLO : LY::VHI);
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off + 8 * LY::VP));
+                const i16x8_t vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                w.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[c], w.o[dt],
+                                                                  0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int D>
+HSAKV_DEV void ltile(LWave<D>& w, const char* buf, int nvalid, float scale_log2) {
+    using LY = LLay<D>;
+    const int lane = threadIdx.x & 63;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    f32x16_t s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = f32x16_t{};
+        const char* kr = buf + (32 * sub + r32) * LY::KP + 16 * g2;
+#pragma unroll
+        for (int ks = 0; ks < LY::KS; ++ks) {
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(kr + LY::KLO + 32 * ks);
+            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, w.qf[ks], s[sub], 0, 0, 0);
+            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, w.qf[ks], s[sub], 0, 0, 0);
+        }
+    }
+    lhalf<D>(w, s[0], buf, 0, nvalid, scale_log2);
+    if (nvalid > 32) lhalf<D>(w, s[1], buf, 1, nvalid, scale_log2);
+}
+
+template <int D>
+__global__ void __launch_bounds__(64 * LW)
+k_lowrank_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_hi,
+                 const bf16_t* __restrict__ v_hi, const bf16_t* __restrict__ k_lo,
+                 const bf16_t* __restrict__ v_lo, float* __restrict__ out) {
+    using LY = LLay<D>;
+    __shared__ __attribute__((aligned(16))) char buf0[LY::BUF];
+    __shared__ __attribute__((aligned(16))) char buf1[LY::BUF];
+    __shared__ __attribute__((aligned(16))) char spare[1024];
+    const int nqb = (g.Lq + LQ - 1) / LQ;
+    const int h = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int query = qb * LQ + 32 * wave + (lane & 31);
+    const bool ok = query < g.Lq;
+    const long long hoff = (long long)h * D;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+
+    LWave<D> w;
+    const bf16_t* qp = q + (long long)(ok ? query : 0) * g.HD + hoff + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < LY::KS; ++ks) w.qf[ks] = ok ? *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks) : bf16x8_t{};
+#pragma unroll
+    for (int dt = 0; dt < LY::DT; ++dt) w.o[dt] = f32x16_t{};
+    w.m = -INFINITY;
+    w.l = 0.f;
+
+    LDma<D> dl;
+    ldma_lanes<D>(dl, wave, 2 * g.HD);
+    const bf16_t* const src[4] = {k_hi + hoff, k_lo + hoff, v_hi + hoff, v_lo + hoff};
+    const uint32_t a0 = lds_addr(buf0), a1 = lds_addr(buf1), asp = lds_addr(spare);
+    const int nt = (g.r + LT - 1) / LT;
+    auto nval = [&](int t) { return g.r - t * LT < LT ? g.r - t * LT : LT; };
+    ldma_tile<D>(a0, asp, src, 0, nval(0), g.HD, dl, wave);
+    for (int t = 0; t < nt; t += 2) {
+        lwait_vmcnt<0>();
+        llds_barrier();
+        if (t + 1 < nt) ldma_tile<D>(a1, asp, src, (long long)(t + 1) * LT, nval(t + 1), g.HD, dl, wave);
+        ltile<D>(w, buf0, nval(t), scale_log2);
+        if (t + 1 >= nt) break;
+        lwait_vmcnt<0>();
+        llds_barrier();
+        if (t + 2 < nt) ldma_tile<D>(a0, asp, src, (long long)(t + 2) * LT, nval(t + 2), g.HD, dl, wave);
+        ltile<D>(w, buf1, nval(t + 1), scale_log2);
+    }
+
+    // O / l for this lane's query: lanes l and l + 32 hold halves of the row sum
+    const float lt = w.l + __shfl_xor(w.l, 32, 64);
+    const float inv_l = lt > 0.f ? 1.0f / lt : 0.f;
+    if (!ok) return;
+    float* dst = out + (long long)query * g.HD + hoff;
+    const int g2 = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < LY::DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            *reinterpret_cast<float4*>(dst + 32 * dt + 8 * a + 4 * g2) =
+                float4{w.o[dt][4 * a] * inv_l, w.o[dt][4 * a + 1] * inv_l, w.o[dt][4 * a + 2] * inv_l,
+                       w.o[dt][4 * a + 3] * inv_l};
+}
+
+}  // namespace
+
+// bf16 low-rank attention (hi + lo K', V'), d = 64 or 128, output float32.
+void launch_lowrank_attn_bf16_mfma32(const Geo& g, const void* q, const void* k_hi, const void* v_hi,
+                                     const void* k_lo, const void* v_lo, float* out, hipStream_t st) {
+    const int nqb = (g.Lq + LQ - 1) / LQ;
+    const dim3 grid(g.H * nqb);
+    if (g.d == 128)
+        hipLaunchKernelGGL(k_lowrank_attn32<128>, grid, dim3(64 * LW), 0, st, g, (const bf16_t*)q,
+                           (const bf16_t*)k_hi, (const bf16_t*)v_hi, (const bf16_t*)k_lo, (const bf16_t*)v_lo, out);
+    else
+        hipLaunchKernelGGL(k_lowrank_attn32<64>, grid, dim3(64 * LW), 0, st, g, (const bf16_t*)q,
+                           (const bf16_t*)k_hi, (const bf16_t*)v_hi, (const bf16_t*)k_lo, (const bf16_t*)v_lo, out);
+}

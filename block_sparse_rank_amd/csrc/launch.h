@@ -54,6 +54,9 @@ void launch_sparse_compute_bf16(const Geo&, const void* q, const void* k_hist, c
 template <typename T>
 void launch_lowrank_attn(const Geo&, const void* q, const void* k_hi, const void* v_hi, const void* k_lo,
                          const void* v_lo, const Epi& ep, hipStream_t);
+// bf16 K', V' (hi + lo pairs), d = 64 or 128: the 32x32x16 MFMA kernel; writes O (float32) to out.
+void launch_lowrank_attn_bf16_mfma32(const Geo&, const void* q, const void* k_hi, const void* v_hi,
+                                     const void* k_lo, const void* v_lo, float* out, hipStream_t);
 
 int lowrank_splits(const Geo&);
 bool proj32_eligible(const Geo&);
