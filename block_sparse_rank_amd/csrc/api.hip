@@ -103,7 +103,8 @@ hipStream_t side_stream() {
 size_t ws_gather(const Geo& g) { return align_up(((size_t)retrieve_slabs(g) + 1) * g.HD * 4); }
 
 size_t ws_select(const Geo& g) {
-    return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4);
+    return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4) +
+           align_up((size_t)g.H * g.NQB * g.NB_max * 4);   // pooled q, pooled k, block logits
 }
 
 size_t ws_sparse(const Geo& g) { return g.elt == 2 ? align_up(sparse_bf16_ws_bytes(g)) : kAlign; }
@@ -153,9 +154,9 @@ void run_gather(const Geo& g, const void* pool_k, const void* pool_v, const floa
 template <typename T>
 void run_select(const Geo& g, const void* q, const void* k_hist, const void* k_intra,
                 const int32_t* n_sel, const TauArg& tau, int32_t* sel_count, int32_t* sel_idx,
-                uint8_t* sel_mask, float* block_mass, float* qb, float* kb, hipStream_t st) {
+                uint8_t* sel_mask, float* block_mass, float* qb, float* kb, float* zl, hipStream_t st) {
     launch_pool<T>(g, q, k_hist, k_intra, n_sel, qb, kb, st);
-    launch_select(g, qb, kb, n_sel, tau, sel_count, sel_idx, sel_mask, block_mass, st);
+    launch_select(g, qb, kb, zl, n_sel, tau, sel_count, sel_idx, sel_mask, block_mass, st);
 }
 
 template <typename T>
@@ -292,14 +293,15 @@ HSAKV_API int hsa_select(const hsakv_dims* dims, const void* q, const void* k_hi
     Carver c{(char*)ws, ws_bytes};
     float* qb = (float*)c.take((size_t)g.H * g.NQB * g.d * 4);
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
+    float* zl = (float*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
     const TauArg t = pack_tau(dims, tau);
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
         run_select<bf16_t>(g, q, k_hist, k_intra, n_sel, t, sel_count, sel_idx, sel_mask,
-                           block_mass, qb, kb, st);
+                           block_mass, qb, kb, zl, st);
     else
         run_select<float>(g, q, k_hist, k_intra, n_sel, t, sel_count, sel_idx, sel_mask,
-                          block_mass, qb, kb, st);
+                          block_mass, qb, kb, zl, st);
     return done();
 }
 
@@ -398,6 +400,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     float* partial = (float*)c.take(ws_gather(g));
     float* qb = (float*)c.take((size_t)g.H * g.NQB * g.d * 4);
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
+    float* zl = (float*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
     void* sparse_ws = c.take(ws_sparse(g));
     int32_t* page_idx = (int32_t*)c.take((size_t)g.Kp * 4);
     int32_t* n_sel = (int32_t*)c.take(4);
@@ -420,7 +423,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
         run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
-                           nullptr, qb, kb, st);
+                           nullptr, qb, kb, zl, st);
         // The sparse plan needs the selection only: it runs on a side stream
         // beside the low-rank branch, and the attention waits for both.
         hipStream_t side = side_stream();
@@ -443,7 +446,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
-                          nullptr, qb, kb, st);
+                          nullptr, qb, kb, zl, st);
         run_linear<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
                           in->F, o_linear, nullptr, nullptr, c, st);
         launch_sparse_attn<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,

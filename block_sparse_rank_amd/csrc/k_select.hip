@@ -276,6 +276,44 @@ k_select(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
 // S is monotone in K, so K* is found by binary search, first over the mass
 // bits, then over the ids that tie on them. No sort and no barrier.
 
+// Block logits for the wave path, as one small GEMM per head on float32 MFMA:
+// Z[h][i][b] = <qb[h][i], kb[h][b]> / sqrt(d) (i < NQB, b < NB), one wave per
+// 32 x 32 tile of (query block, key block) pairs, v_mfma_f32_32x32x2_f32 over
+// d. Lane l feeds A[i = l % 32][k] and B[k][b = l % 32] for the k its half
+// (l / 32) takes in each product; any assignment of the d terms to products
+// gives the same dot product.
+__global__ void __launch_bounds__(256)
+k_block_logits(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
+               const int32_t* __restrict__ n_sel_p, float* __restrict__ z) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int mt = (g.NQB + 31) / 32, nt = (g.NB_max + 31) / 32;
+    const int tile = blockIdx.x * 4 + wave;
+    if (tile >= g.H * mt * nt) return;
+    const int h = tile / (mt * nt), rem = tile % (mt * nt), ti = rem / nt, tb = rem % nt;
+    const int NB = hist_blocks(g, *n_sel_p) + g.NBc;
+    if (tb * 32 >= NB) return;
+    const int r32 = lane & 31, g2 = lane >> 5;
+    const int ia = ti * 32 + r32 < g.NQB ? ti * 32 + r32 : g.NQB - 1;
+    const int ba = tb * 32 + r32 < NB ? tb * 32 + r32 : NB - 1;
+    const float* qa = qb + ((size_t)h * g.NQB + ia) * g.d;
+    const float* kr = kb + ((size_t)h * g.NB_max + ba) * g.d;
+    f32x16_t acc = f32x16_t{};
+    for (int t = 0; t < g.d; t += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(qa + t);
+        const float4 b = *reinterpret_cast<const float4*>(kr + t);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g2 ? a.y : a.x, g2 ? b.y : b.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g2 ? a.w : a.z, g2 ? b.w : b.z, acc, 0, 0, 0);
+    }
+    // element e of lane l: query block 8 (e / 4) + 4 (l / 32) + e % 4, key block l % 32
+    const float inv_sqrt_d = 1.0f / sqrtf((float)g.d);
+    const int b = tb * 32 + r32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int i = ti * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (i < g.NQB && b < NB) z[((size_t)h * g.NQB + i) * g.NB_max + b] = acc[e] * inv_sqrt_d;
+    }
+}
+
 HSAKV_DEV float masked_sum(const float* p, const unsigned* mb, int NPL_, unsigned M, int I,
                            bool use_id, int lane) {
     float acc = 0.f;
@@ -289,45 +327,25 @@ HSAKV_DEV float masked_sum(const float* p, const unsigned* mb, int NPL_, unsigne
 
 template <int NPL>
 __global__ void __launch_bounds__(256)
-k_select_wave(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
-              const int32_t* __restrict__ n_sel_p, TauArg tau, int32_t* __restrict__ sel_count,
-              int32_t* __restrict__ sel_idx, uint8_t* __restrict__ sel_mask,
+k_select_wave(Geo g, const float* __restrict__ zl, const int32_t* __restrict__ n_sel_p, TauArg tau,
+              int32_t* __restrict__ sel_count, int32_t* __restrict__ sel_idx, uint8_t* __restrict__ sel_mask,
               float* __restrict__ block_mass) {
-    __shared__ float qrow_s[4][128];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * 4 + wave;
-    const bool live = row < g.H * g.NQB;
-    const int h = live ? row / g.NQB : 0;
-    const int i = live ? row % g.NQB : 0;
+    if (row >= g.H * g.NQB) return;
+    const int h = row / g.NQB;
+    const int i = row % g.NQB;
     const int n_sel = *n_sel_p;
     const int NB = hist_blocks(g, n_sel) + g.NBc;
-    float* qrow = qrow_s[wave];
-    for (int e = lane; e < g.d; e += 64) qrow[e] = live ? qb[((size_t)h * g.NQB + i) * g.d + e] : 0.f;
-    __syncthreads();
-    if (!live) return;
 
-    // pooled logits, one block per lane and item
-    const float inv_sqrt_d = 1.0f / sqrtf((float)g.d);
-    const float* kbh = kb + (size_t)h * g.NB_max * g.d;
+    // the row's pooled logits (k_block_logits), one block per lane and item
+    const float* zr = zl + ((size_t)h * g.NQB + i) * g.NB_max;
     float p[NPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int b = lane + 64 * j;
-        float z = -INFINITY;
-        if (b < NB) {
-            const float4* kr = reinterpret_cast<const float4*>(kbh + (size_t)b * g.d);
-            const float4* qr = reinterpret_cast<const float4*>(qrow);
-            float s = 0.f;
-            for (int e = 0; e < g.d / 4; ++e) {
-                const float4 kv = kr[e], qv = qr[e];
-                s = fmaf(qv.x, kv.x, s);
-                s = fmaf(qv.y, kv.y, s);
-                s = fmaf(qv.z, kv.z, s);
-                s = fmaf(qv.w, kv.w, s);
-            }
-            z = s * inv_sqrt_d;
-        }
+        const float z = b < NB ? zr[b] : -INFINITY;
         p[j] = z;
         mx = fmaxf(mx, z);
     }
@@ -394,15 +412,17 @@ k_select_wave(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
     if (lane == 0) sel_count[(size_t)h * g.NQB + i] = pos;
 }
 
-void launch_select(const Geo& g, const float* qb, const float* kb, const int32_t* n_sel,
+void launch_select(const Geo& g, const float* qb, const float* kb, float* zl, const int32_t* n_sel,
                    const TauArg& tau_dev, int32_t* sel_count, int32_t* sel_idx, uint8_t* sel_mask,
                    float* block_mass, hipStream_t st) {
     const int rows = g.H * g.NQB;
     const int per_lane = (g.NB_max + 63) / 64;
-    if (g.d <= 128 && per_lane <= 32) {
+    if (g.d <= 128 && g.d % 4 == 0 && per_lane <= 32) {
+        const int tiles = g.H * ((g.NQB + 31) / 32) * ((g.NB_max + 31) / 32);
+        hipLaunchKernelGGL(k_block_logits, dim3((tiles + 3) / 4), dim3(256), 0, st, g, qb, kb, n_sel, zl);
         const dim3 grid((rows + 3) / 4);
 #define HSAKV_SEL(NPL)                                                                            \
-    hipLaunchKernelGGL(k_select_wave<NPL>, grid, dim3(256), 0, st, g, qb, kb, n_sel, tau_dev,      \
+    hipLaunchKernelGGL(k_select_wave<NPL>, grid, dim3(256), 0, st, g, (const float*)zl, n_sel, tau_dev, \
                        sel_count, sel_idx, sel_mask, block_mass)
         if (per_lane <= 2) HSAKV_SEL(2);
         else if (per_lane <= 8) HSAKV_SEL(8);

@@ -31,7 +31,7 @@ void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* po
 template <typename T>
 void launch_pool(const Geo&, const void* q, const void* k_hist, const void* k_intra, const int32_t* n_sel,
                  float* qb, float* kb, hipStream_t);
-void launch_select(const Geo&, const float* qb, const float* kb, const int32_t* n_sel, const TauArg& tau,
+void launch_select(const Geo&, const float* qb, const float* kb, float* zl, const int32_t* n_sel, const TauArg& tau,
                    int32_t* sel_count, int32_t* sel_idx, uint8_t* sel_mask, float* block_mass, hipStream_t);
 
 template <typename T>
