@@ -57,11 +57,21 @@ k_pool(Geo g, const T* __restrict__ q, const T* __restrict__ k_hist, const T* __
     const int col0 = (blockIdx.y * 32 + lane) * 8; // first of 8 columns
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (col0 < g.HD) {
-        for (long long t = t0 + grp; t < t1; t += 8) {
-            float v[8];
-            Elt<T>::load8(src + t * g.HD + col0, v);
+        // four tokens of this group in flight at a time; the sum order is
+        // still token order within the group
+        for (long long t = t0 + grp; t < t1; t += 32) {
+            float v[4][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += v[e];
+            for (int u = 0; u < 4; ++u) {
+                const long long tu = t + 8 * u < t1 ? t + 8 * u : t;
+                Elt<T>::load8(src + tu * g.HD + col0, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (t + 8 * u < t1) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+                }
         }
     }
     __shared__ float part[8][32 * 8 + 4];
@@ -279,9 +289,10 @@ k_select(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
 // Block logits for the wave path, as one small GEMM per head on float32 MFMA:
 // Z[h][i][b] = <qb[h][i], kb[h][b]> / sqrt(d) (i < NQB, b < NB), one wave per
 // 32 x 32 tile of (query block, key block) pairs, v_mfma_f32_32x32x2_f32 over
-// d. Lane l feeds A[i = l % 32][k] and B[k][b = l % 32] for the k its half
-// (l / 32) takes in each product; any assignment of the d terms to products
-// gives the same dot product.
+// d. Lane l feeds A[i = l % 32][k] and B[k][b = l % 32] for the d term its
+// half (l / 32) takes in each product; any assignment of the d terms to
+// products gives the same dot product.
+template <int D>
 __global__ void __launch_bounds__(256)
 k_block_logits(Geo g, const float* __restrict__ qb, const float* __restrict__ kb,
                const int32_t* __restrict__ n_sel_p, float* __restrict__ z) {
@@ -295,17 +306,27 @@ k_block_logits(Geo g, const float* __restrict__ qb, const float* __restrict__ kb
     const int r32 = lane & 31, g2 = lane >> 5;
     const int ia = ti * 32 + r32 < g.NQB ? ti * 32 + r32 : g.NQB - 1;
     const int ba = tb * 32 + r32 < NB ? tb * 32 + r32 : NB - 1;
-    const float* qa = qb + ((size_t)h * g.NQB + ia) * g.d;
-    const float* kr = kb + ((size_t)h * g.NB_max + ba) * g.d;
+    const float* qa = qb + ((size_t)h * g.NQB + ia) * D;
+    const float* kr = kb + ((size_t)h * g.NB_max + ba) * D;
     f32x16_t acc = f32x16_t{};
-    for (int t = 0; t < g.d; t += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(qa + t);
-        const float4 b = *reinterpret_cast<const float4*>(kr + t);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g2 ? a.y : a.x, g2 ? b.y : b.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g2 ? a.w : a.z, g2 ? b.w : b.z, acc, 0, 0, 0);
+    // 32 d-values of each operand in flight at a time
+    // products 2u, 2u + 1 take d = 4u + 2 (l / 32) and the one after it
+#pragma unroll
+    for (int t0 = 0; t0 < D; t0 += 32) {
+        float2 a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a[u] = *reinterpret_cast<const float2*>(qa + t0 + 4 * u + 2 * g2);
+            b[u] = *reinterpret_cast<const float2*>(kr + t0 + 4 * u + 2 * g2);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u].x, b[u].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u].y, b[u].y, acc, 0, 0, 0);
+        }
     }
     // element e of lane l: query block 8 (e / 4) + 4 (l / 32) + e % 4, key block l % 32
-    const float inv_sqrt_d = 1.0f / sqrtf((float)g.d);
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     const int b = tb * 32 + r32;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -417,9 +438,12 @@ void launch_select(const Geo& g, const float* qb, const float* kb, float* zl, co
                    float* block_mass, hipStream_t st) {
     const int rows = g.H * g.NQB;
     const int per_lane = (g.NB_max + 63) / 64;
-    if (g.d <= 128 && g.d % 4 == 0 && per_lane <= 32) {
+    if ((g.d == 64 || g.d == 128) && per_lane <= 32) {
         const int tiles = g.H * ((g.NQB + 31) / 32) * ((g.NB_max + 31) / 32);
-        hipLaunchKernelGGL(k_block_logits, dim3((tiles + 3) / 4), dim3(256), 0, st, g, qb, kb, n_sel, zl);
+        if (g.d == 128)
+            hipLaunchKernelGGL(k_block_logits<128>, dim3((tiles + 3) / 4), dim3(256), 0, st, g, qb, kb, n_sel, zl);
+        else
+            hipLaunchKernelGGL(k_block_logits<64>, dim3((tiles + 3) / 4), dim3(256), 0, st, g, qb, kb, n_sel, zl);
         const dim3 grid((rows + 3) / 4);
 #define HSAKV_SEL(NPL)                                                                            \
     hipLaunchKernelGGL(k_select_wave<NPL>, grid, dim3(256), 0, st, g, (const float*)zl, n_sel, tau_dev, \
