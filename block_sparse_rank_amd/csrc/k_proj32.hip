@@ -256,8 +256,12 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 // L2 reads of 128 x 128 tiles), 8 waves (wave w: rows 128 (w % 2), columns
 // 64 (w / 2), eight 32x32 accumulators), one work-group per CU and a ring of
 // four LDS stages, three in flight, so the stream keeps enough bytes in
-// flight. Rows are padded for conflict-free operand reads: X 5 slots (80 B,
-// the 16 rows of one b128 read phase on distinct banks), Y 36 slots (576 B).
+// flight. The 16-byte chunks of a row are XOR-swizzled in LDS for
+// conflict-free operand reads, with rows unpadded so every DMA lane loads
+// data and each row's bytes stay contiguous: X (64-byte rows) slot s of row r
+// holds chunk s ^ (r / 4 mod 4), so the 16 rows of one b128 read phase fall
+// on distinct banks; Y (512-byte rows) slot s of row r holds chunk
+// s ^ 4 (r mod 4), so the 4 rows x 4 chunks of a transpose read's 32 lanes do.
 //
 // The k-steps of a split run over its history part, then its chunk part, each
 // ending in a partial step, so no step straddles the seam. The DMA goes
@@ -265,20 +269,21 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 // past the part's end, or an X column past the end of E, is out of range and
 // not read; its LDS row is zeroed before use.
 constexpr int WM = 256, WN = 256, WK = 32, WT = 512, WWV = 8, WSTAGES = 4;
-constexpr int WA_SLOTS = WK / 8 + 1;           // 5
-constexpr int WB_SLOTS = WN / 8 + 4;           // 36
-constexpr int WA_ROWB = WA_SLOTS * 16;         // 80
-constexpr int WB_ROWB = WB_SLOTS * 16;         // 576
-constexpr int WA_BYTES = WM * WA_ROWB;         // 20480
-constexpr int WB_BYTES = WK * WB_ROWB;         // 18432
-constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 38912; four stages 155648 bytes
-constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 20
-constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 18
-constexpr int W_PER = 5;                       // DMA instructions per wave and k-step
-constexpr int W_SPARE = 2048;                  // LDS target of the two idle instructions
+constexpr int WA_SLOTS = WK / 8;               // 4 chunks per X row
+constexpr int WB_SLOTS = WN / 8;               // 32 chunks per Y row
+constexpr int WA_ROWB = WA_SLOTS * 16;         // 64
+constexpr int WB_ROWB = WB_SLOTS * 16;         // 512
+constexpr int WA_BYTES = WM * WA_ROWB;         // 16384
+constexpr int WB_BYTES = WK * WB_ROWB;         // 16384
+constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 32768; four stages 131072 bytes
+constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 16
+constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 16
+constexpr int W_PER = 4;                       // DMA instructions per wave and k-step
 static_assert(WM * WA_SLOTS % 64 == 0 && WK * WB_SLOTS % 64 == 0, "whole wave instructions");
 static_assert(WA_BYTES == WA_INSTR * 1024, "Y follows X in instruction order");
-static_assert(WA_INSTR + WB_INSTR + 2 == WWV * W_PER, "38 DMA instructions plus two idle ones");
+static_assert(WA_INSTR + WB_INSTR == WWV * W_PER, "every wave sends the same count");
+HSAKV_DEV int xswz(int row) { return (row >> 2) & 3; }   // X chunk swizzle
+HSAKV_DEV int yswz(int row) { return 4 * (row & 3); }    // Y chunk swizzle
 
 // Raw buffer resource: base p, `bytes` in range, 32-bit untyped data.
 HSAKV_DEV __amdgpu_buffer_rsrc_t w_rsrc(const bf16_t* p, long long bytes) {
@@ -305,9 +310,9 @@ HSAKV_DEV void wait_vm() {
 HSAKV_DEV void w_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Byte offsets of this wave's DMA instructions j = wave + 8 q (fixed over
-// the k-steps): X (j < 20) m * L + 8 * slot from the step's first column,
-// Y (20 <= j < 38) row * HD + n0 + 8 * slot from the step's first row; pad
-// lanes load slot 0 of their row.
+// the k-steps): X (j < 16) m * L + 8 chunk from the step's first column,
+// Y (j >= 16) row * HD + n0 + 8 chunk from the step's first row, the chunk a
+// lane's LDS slot holds under the swizzle.
 HSAKV_DEV void w_lanes(uint32_t (&off)[W_PER], const Geo& g, int wave, int m0, int n0) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -316,9 +321,9 @@ HSAKV_DEV void w_lanes(uint32_t (&off)[W_PER], const Geo& g, int wave, int m0, i
         const int La = j * 64 + lane, Lb = (j - WA_INSTR) * 64 + lane;
         const int ra = La / WA_SLOTS, sa = La % WA_SLOTS, rb = Lb / WB_SLOTS, sb = Lb % WB_SLOTS;
         const int m = m0 + ra < g.r ? m0 + ra : g.r - 1;
-        const uint32_t oa = 2u * (uint32_t)(m * (int)g.L + (sa < WK / 8 ? sa : 0) * 8);
-        const uint32_t ob = 2u * (uint32_t)(rb * g.HD + n0 + (sb < WN / 8 ? sb : 0) * 8);
-        off[q] = j < WA_INSTR ? oa : (j < WA_INSTR + WB_INSTR ? ob : 0u);
+        const uint32_t oa = 2u * (uint32_t)(m * (int)g.L + (sa ^ xswz(ra)) * 8);
+        const uint32_t ob = 2u * (uint32_t)(rb * g.HD + n0 + (sb ^ yswz(rb)) * 8);
+        off[q] = j < WA_INSTR ? oa : ob;
     }
 }
 
@@ -339,30 +344,37 @@ HSAKV_DEV void w_compute(const char* buf, f32x16_t (&acc)[4][2], int wave) {
     const int lane = threadIdx.x & 63;
     const int mw = wave & 1, nw = wave >> 1;
     const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
-    const char* A = buf + (128 * mw + r32) * WA_ROWB + 16 * g2;
-    const char* B = buf + WA_BYTES + (8 * (G >> 1) + (j >> 2)) * WB_ROWB + (64 * nw + 16 * (G & 1) + 4 * (j & 3)) * 2;
-    const uint32_t bb = (uint32_t)(uintptr_t)(const lds_i16x4_t*)B;
+    // X row 128 mw + 32 mt + r32 has swizzle xswz(r32); chunk 2 kk + g2 sits in slot (2 kk + g2) ^ xswz
+    const char* Arow = buf + (128 * mw + r32) * WA_ROWB;
+    const char* A0 = Arow + 16 * (g2 ^ xswz(r32));
+    const char* A1 = Arow + 16 * ((2 + g2) ^ xswz(r32));
+    // Y rows 16 kk + 4 h + 8 (G / 2) + j / 4 have swizzle yswz(j / 4); the 8 columns of
+    // chunk 8 nw + 4 nt + 2 (G & 1) + (j & 3) / 2 sit in slot chunk ^ yswz, at byte 8 (j & 1)
+    const int cy = 8 * nw + 2 * (G & 1) + ((j & 3) >> 1);
+    const char* Brow = buf + WA_BYTES + (8 * (G >> 1) + (j >> 2)) * WB_ROWB + 8 * (j & 1);
+    const uint32_t bb0 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * (cy ^ yswz(j >> 2)));
+    const uint32_t bb1 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * ((cy + 4) ^ yswz(j >> 2)));
     // r[4 kk + 2 nt + h]: k rows 16 kk + 4 h (+ 8 (G / 2) + j / 4), columns 32 nt + ...
     constexpr int H = 4 * WB_ROWB, K1 = 16 * WB_ROWB;
     bf16x8_t a0[4], a1[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) a0[mt] = *reinterpret_cast<const bf16x8_t*>(A + 32 * mt * WA_ROWB);
+    for (int mt = 0; mt < 4; ++mt) a0[mt] = *reinterpret_cast<const bf16x8_t*>(A0 + 32 * mt * WA_ROWB);
     w_u32x2_t r[8];
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %3, %8 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:%14\n\t"
-        "ds_read_b64_tr_b16 %7, %8 offset:%15\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %6, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(bb), "i"(H), "i"(64), "i"(64 + H), "i"(K1), "i"(K1 + H), "i"(K1 + 64), "i"(K1 + 64 + H)
+        : "v"(bb0), "v"(bb1), "i"(H), "i"(K1), "i"(K1 + H)
         : "memory");
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) a1[mt] = *reinterpret_cast<const bf16x8_t*>(A + 32 * mt * WA_ROWB + 32);
+    for (int mt = 0; mt < 4; ++mt) a1[mt] = *reinterpret_cast<const bf16x8_t*>(A1 + 32 * mt * WA_ROWB);
     bf16x8_t b[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -387,7 +399,7 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
                   const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
                   const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
                   const int32_t* __restrict__ n_sel_p, int nsplit, int per_xcd, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) char ring[WSTAGES * WSTAGE + W_SPARE];
+    __shared__ __attribute__((aligned(16))) char ring[WSTAGES * WSTAGE];
     const int MT = (g.r + WM - 1) / WM, NTL = g.HD / WN;
     const int total = nsplit * 2 * MT * NTL;
     const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -416,7 +428,6 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
 
     uint32_t off[W_PER];
     w_lanes(off, g, wave, m0, n0);
-    const __amdgpu_buffer_rsrc_t r_idle = w_rsrc(X, 0);
     const long long xbytes = 2LL * g.r * g.L;
 
     // Send k-step s into its ring stage: per instruction a uniform resource
@@ -435,8 +446,8 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
 #pragma unroll
         for (int q = 0; q < W_PER; ++q) {
             const int j = wave + WWV * q;
-            const __amdgpu_buffer_rsrc_t rs = j < WA_INSTR ? rx : (j < WA_INSTR + WB_INSTR ? ry : r_idle);
-            char* dst = j < WA_INSTR + WB_INSTR ? buf + j * 1024 : ring + WSTAGES * WSTAGE + (j & 1) * 1024;
+            const __amdgpu_buffer_rsrc_t rs = j < WA_INSTR ? rx : ry;
+            char* dst = buf + j * 1024;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, w_dst(dst), 16, off[q], 0, 0, 0);
         }
     };
