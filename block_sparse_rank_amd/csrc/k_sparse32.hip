@@ -516,7 +516,9 @@ k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restri
                 const uint32_t bw = (uint32_t)__builtin_amdgcn_readlane((int)v, pl_);
                 uni[x] = r == 0 ? bw : (uni[x] | bw);
             }
-            if (lane == pl_) left[pk] = false;
+#pragma unroll
+            for (int k = 0; k < kGroupRowsPerLane; ++k)
+                if (k == pk && lane == pl_) left[k] = false;   // fixed indices: `left` stays in registers
         }
     }
 }
