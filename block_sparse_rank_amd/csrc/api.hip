@@ -422,22 +422,23 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     if (eb == 2) {
         run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
-        run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
-                           nullptr, qb, kb, zl, st);
-        // The sparse plan needs the selection only: it runs on a side stream
-        // beside the low-rank branch, and the attention waits for both.
+        // The low-rank branch needs the gathered KV only: it runs on a side
+        // stream beside the pooling, the block selection and the sparse plan
+        // (small, latency-bound kernels), and the attention waits for both.
         hipStream_t side = side_stream();
         hipEvent_t fork = nullptr, join = nullptr;
         const bool split = side && side != st &&
                            hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
                            hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
                            hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
-        launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, sparse_ws, split ? side : st);
-        const bool joined = split && hipEventRecord(join, side) == hipSuccess;
         run_linear<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
-                           in->F, o_linear, nullptr, nullptr, c, st);
+                           in->F, o_linear, nullptr, nullptr, c, split ? side : st);
+        const bool joined = split && hipEventRecord(join, side) == hipSuccess;
+        run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
+                           nullptr, qb, kb, zl, st);
+        launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, sparse_ws, st);
         if (joined) (void)hipStreamWaitEvent(st, join, 0);
-        else if (split) (void)hipStreamSynchronize(side);   // plan enqueued but not joined: finish it
+        else if (split) (void)hipStreamSynchronize(side);   // branch enqueued but not joined: finish it
         launch_sparse_compute_bf16(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, sparse_ws, ep,
                                    st);
         if (fork) (void)hipEventDestroy(fork);

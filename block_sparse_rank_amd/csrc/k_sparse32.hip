@@ -816,12 +816,18 @@ k_sparse_attn32(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
 }
 
 // Groups split between work-groups: merge the segment partials in range order,
-// then the same epilogue. Groups without tiles get O = 0.
+// then the same epilogue. Groups without tiles get O = 0. One work-group per
+// (group, row wave) and one wave per 32-row tile of O^T: a thread holds 16
+// outputs, so many waves keep their partial loads in flight at once. The
+// gate's dot product is split over the waves (two 16-wide column steps each)
+// and added in wave order through LDS.
 template <int D>
-__global__ void __launch_bounds__(64 * NW)
+__global__ void __launch_bounds__(64 * Wave<D>::DT)
 k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict__ gtiles,
                  const int32_t* __restrict__ gstart, PlanArgs pl, Epi ep) {
-    const int grp = blockIdx.x;
+    constexpr int DT = Wave<D>::DT;
+    const int grp = blockIdx.x, wave = blockIdx.y;
+    const int dt = threadIdx.x >> 6, lane = threadIdx.x & 63, g2 = lane >> 5;
     const int T = gstart[pl.NG];
     const int S = gstart[grp], Tg = gtiles[grp];
     const int G = pl.G;
@@ -834,10 +840,29 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
         if (range_start(k0 + 1, T, G) >= S + Tg) return;   // one range holds the whole group
     }
     const int gph = groups_per_head(g);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int h = grp / gph, i = pl.grows[grp * R + (wave >> 1)];
-    Wave<D> w;
-    start_rows<D>(g, q, h, i, w);
+    const int query = i * g.Bq + 32 * (wave & 1) + (lane & 31);
+    const bool ok = i < g.NQB && query < g.Lq;
+    __shared__ float gpart[DT][64];
+    if (ep.out) {
+        float dot = 0.f;
+        if (ok) {
+            const bf16_t* qp = q + (long long)query * g.HD + (long long)h * D + 8 * g2;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ks = 2 * dt + u;
+                const bf16x8_t qv = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    dot = fmaf((float)qv[e], ep.w_g[h * D + 16 * ks + 8 * g2 + e], dot);
+            }
+        }
+        gpart[dt][lane] = dot;
+    }
+    float o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = 0.f;
+    float m = -INFINITY, l = 0.f;
     if (Tg > 0) {
         for (int kk = k0; kk < G; ++kk) {
             const int s0 = range_start(kk, T, G);
@@ -845,26 +870,57 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
             if (range_start(kk + 1, T, G) == s0) continue;   // empty range
             const int slot = 2 * kk + (s0 < S ? 1 : 0);
             const float2 ml = pl.part_ml[((size_t)slot * NW + wave) * 64 + lane];
-            const float m_new = fmaxf(w.m, ml.x);
-            const float a_old = w.m == -INFINITY ? 0.f : exp2f(w.m - m_new);
+            const float4* po = reinterpret_cast<const float4*>(pl.part_o + part_index<D>(slot, wave, dt, lane));
+            float4 v[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = po[c];
+            const float m_new = fmaxf(m, ml.x);
+            const float a_old = m == -INFINITY ? 0.f : exp2f(m - m_new);
             const float a_seg = ml.x == -INFINITY ? 0.f : exp2f(ml.x - m_new);
-            w.m = m_new;
-            w.l = w.l * a_old + ml.y * a_seg;
+            m = m_new;
+            l = l * a_old + ml.y * a_seg;
 #pragma unroll
-            for (int dt = 0; dt < Wave<D>::DT; ++dt) {
-                const float4* po = reinterpret_cast<const float4*>(pl.part_o + part_index<D>(slot, wave, dt, lane));
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const float4 v = po[c];
-                    w.o[dt][4 * c] = w.o[dt][4 * c] * a_old + v.x * a_seg;
-                    w.o[dt][4 * c + 1] = w.o[dt][4 * c + 1] * a_old + v.y * a_seg;
-                    w.o[dt][4 * c + 2] = w.o[dt][4 * c + 2] * a_old + v.z * a_seg;
-                    w.o[dt][4 * c + 3] = w.o[dt][4 * c + 3] * a_old + v.w * a_seg;
-                }
+            for (int c = 0; c < 4; ++c) {
+                o[4 * c] = o[4 * c] * a_old + v[c].x * a_seg;
+                o[4 * c + 1] = o[4 * c + 1] * a_old + v[c].y * a_seg;
+                o[4 * c + 2] = o[4 * c + 2] * a_old + v[c].z * a_seg;
+                o[4 * c + 3] = o[4 * c + 3] * a_old + v[c].w * a_seg;
             }
         }
     }
-    finish_rows<D>(g, ep, h, i, w);
+    float gate = 0.f;
+    if (ep.out) {
+        __syncthreads();
+        float dot = gpart[0][lane];
+#pragma unroll
+        for (int k = 1; k < DT; ++k) dot += gpart[k][lane];
+        dot += __shfl_xor(dot, 32, 64);
+        const float x = dot + ep.b_g[h];
+        const float z = expf(-fabsf(x));
+        gate = x >= 0.f ? 1.0f / (1.0f + z) : z / (1.0f + z);
+    }
+    const float lt = l + __shfl_xor(l, 32, 64);
+    const float inv_l = lt > 0.f ? 1.0f / lt : 0.f;
+    if (!ok) return;
+    const long long base = (long long)query * g.HD + (long long)h * D;
+    if (ep.gate && g2 == 0 && dt == 0) ep.gate[(long long)query * g.H + h] = gate;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * dt + 8 * a + 4 * g2;
+        const float4 r = {o[4 * a] * inv_l, o[4 * a + 1] * inv_l, o[4 * a + 2] * inv_l, o[4 * a + 3] * inv_l};
+        if (ep.o_main) *reinterpret_cast<float4*>(ep.o_main + base + d0) = r;
+        if (ep.out) {
+            const float4 lin = *reinterpret_cast<const float4*>(ep.o_lin + base + d0);
+            const float r0 = gate * r.x + (1.f - gate) * lin.x;
+            const float r1 = gate * r.y + (1.f - gate) * lin.y;
+            const float r2 = gate * r.z + (1.f - gate) * lin.z;
+            const float r3 = gate * r.w + (1.f - gate) * lin.w;
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16(r0) | ((uint32_t)f32_to_bf16(r1) << 16);
+            pk.y = (uint32_t)f32_to_bf16(r2) | ((uint32_t)f32_to_bf16(r3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(ep.out) + base + d0) = pk;
+        }
+    }
 }
 
 // Attention work-groups on the current device: one per CU, at most kSparseMaxWg.
@@ -951,7 +1007,7 @@ void launch_compute_d(const Geo& g, const void* q, const void* k_hist, const voi
                        (const bf16_t*)v_intra, n_sel, (const int2*)s.tdesc, tiles_per_group(g),
                        (const int32_t*)s.gcount, (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl,
                        per_xcd, ep);
-    hipLaunchKernelGGL((k_sparse_combine<D>), dim3(NG), dim3(64 * NW), 0, st, g, (const bf16_t*)q,
+    hipLaunchKernelGGL((k_sparse_combine<D>), dim3(NG, NW), dim3(64 * Wave<D>::DT), 0, st, g, (const bf16_t*)q,
                        (const int32_t*)s.gtiles, (const int32_t*)s.gstart, pl, ep);
 }
 
