@@ -62,6 +62,8 @@ int check_dims(const hsakv_dims* d) {
     if (d->P > 65536) return HSAKV_ERR_UNSUPPORTED;
     Geo g = make_geo(d);
     if (g.NB_max > 4096) return HSAKV_ERR_UNSUPPORTED;
+    // one-dimensional grids of (block, 256 columns) work-groups stay below 2^32 threads
+    if ((long long)(g.NQB + g.NB_max) * ((g.HD + 255) / 256) * 256 >= (1LL << 32)) return HSAKV_ERR_UNSUPPORTED;
     if (retrieve_smem_bytes(g) > 65536) return HSAKV_ERR_UNSUPPORTED;
     return HSAKV_OK;
 }
@@ -145,17 +147,21 @@ struct Carver {
 template <typename T>
 void run_gather(const Geo& g, const void* pool_k, const void* pool_v, const float* page_kmean,
                 const int32_t* page_prompt, int cur_prompt, const void* q, int32_t* page_idx,
-                int32_t* n_sel, void* k_hist, void* v_hist, float* partial, hipStream_t st) {
+                int32_t* n_sel, void* k_hist, void* v_hist, float* partial, float* kb, hipStream_t st) {
     launch_q_partials<T>(g, q, partial, st);
     launch_retrieve(g, partial, page_kmean, page_prompt, cur_prompt, page_idx, n_sel, st);
-    launch_gather(g, (int)sizeof(T), pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, st);
+    if (kb)   // the history blocks of the pooled keys come with the copy
+        launch_gather_pool<T>(g, pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, kb, st);
+    else
+        launch_gather(g, (int)sizeof(T), pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, st);
 }
 
 template <typename T>
 void run_select(const Geo& g, const void* q, const void* k_hist, const void* k_intra,
                 const int32_t* n_sel, const TauArg& tau, int32_t* sel_count, int32_t* sel_idx,
-                uint8_t* sel_mask, float* block_mass, float* qb, float* kb, float* zl, hipStream_t st) {
-    launch_pool<T>(g, q, k_hist, k_intra, n_sel, qb, kb, st);
+                uint8_t* sel_mask, float* block_mass, float* qb, float* kb, float* zl, bool hist_pooled,
+                hipStream_t st) {
+    launch_pool<T>(g, q, k_hist, k_intra, n_sel, qb, kb, hist_pooled, st);
     launch_select(g, qb, kb, zl, n_sel, tau, sel_count, sel_idx, sel_mask, block_mass, st);
 }
 
@@ -271,10 +277,10 @@ HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void*
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
         run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, q, page_idx,
-                           n_sel, k_hist, v_hist, (float*)ws, st);
+                           n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     else
         run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, q, page_idx,
-                          n_sel, k_hist, v_hist, (float*)ws, st);
+                          n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     return done();
 }
 
@@ -298,10 +304,10 @@ HSAKV_API int hsa_select(const hsakv_dims* dims, const void* q, const void* k_hi
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
         run_select<bf16_t>(g, q, k_hist, k_intra, n_sel, t, sel_count, sel_idx, sel_mask,
-                           block_mass, qb, kb, zl, st);
+                           block_mass, qb, kb, zl, false, st);
     else
         run_select<float>(g, q, k_hist, k_intra, n_sel, t, sel_count, sel_idx, sel_mask,
-                          block_mass, qb, kb, zl, st);
+                          block_mass, qb, kb, zl, false, st);
     return done();
 }
 
@@ -421,7 +427,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     hipStream_t st = (hipStream_t)stream;
     if (eb == 2) {
         run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
-                           in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
+                           in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         // The low-rank branch needs the gathered KV only: it runs on a side
         // stream beside the pooling, the block selection and the sparse plan
         // (small, latency-bound kernels), and the attention waits for both.
@@ -435,7 +441,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
                            in->F, o_linear, nullptr, nullptr, c, split ? side : st);
         const bool joined = split && hipEventRecord(join, side) == hipSuccess;
         run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
-                           nullptr, qb, kb, zl, st);
+                           nullptr, qb, kb, zl, true, st);
         launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, sparse_ws, st);
         if (joined) (void)hipStreamWaitEvent(st, join, 0);
         else if (split) (void)hipStreamSynchronize(side);   // branch enqueued but not joined: finish it
@@ -445,9 +451,9 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         if (join) (void)hipEventDestroy(join);
     } else {
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
-                          in->q, page_idx, n_sel, k_hist, v_hist, partial, st);
+                          in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
-                          nullptr, qb, kb, zl, st);
+                          nullptr, qb, kb, zl, true, st);
         run_linear<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
                           in->F, o_linear, nullptr, nullptr, c, st);
         launch_sparse_attn<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,

@@ -223,6 +223,120 @@ k_gather(const u32x4* __restrict__ pool_k, const u32x4* __restrict__ pool_v,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gather with the history K pooled on the way (the forward's variant): one
+// work-group per (history block of Binter rows, 256 columns, K or V), the
+// column slabs of a block adjacent in launch order so that the work-groups
+// running together read whole rows. Rows are
+// copied bit for bit; for K each thread also sums its 8 columns over the rows
+// grp, grp + 8, ... of the block in row order, and the eight row groups are
+// added in group order: the same float32 operations as the pooling of a
+// gathered block, so both give the same pooled key.
+
+template <typename T> struct Row8;
+template <> struct Row8<bf16_t> {
+    u32x4 a;
+    HSAKV_DEV void load(const bf16_t* p) { a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+    HSAKV_DEV void store(bf16_t* p) const { *reinterpret_cast<u32x4*>(p) = a; }
+    HSAKV_DEV void add_to(float* acc) const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(w[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Row8<float> {
+    u32x4 a, b;
+    HSAKV_DEV void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+    }
+    HSAKV_DEV void store(float* p) const {
+        reinterpret_cast<u32x4*>(p)[0] = a;
+        reinterpret_cast<u32x4*>(p)[1] = b;
+    }
+    HSAKV_DEV void add_to(float* acc) const {
+        acc[0] += __uint_as_float(a.x); acc[1] += __uint_as_float(a.y);
+        acc[2] += __uint_as_float(a.z); acc[3] += __uint_as_float(a.w);
+        acc[4] += __uint_as_float(b.x); acc[5] += __uint_as_float(b.y);
+        acc[6] += __uint_as_float(b.z); acc[7] += __uint_as_float(b.w);
+    }
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
+              const int32_t* __restrict__ page_idx, const int32_t* __restrict__ n_sel_p,
+              T* __restrict__ k_hist, T* __restrict__ v_hist, float* __restrict__ kb) {
+    constexpr int kRows = sizeof(T) == 2 ? 16 : 8;   // rows in flight per thread
+    const int n_sel = *n_sel_p;
+    const int nslab = (g.HD + 255) / 256;
+    const int b = blockIdx.x / nslab, slab = blockIdx.x - b * nslab;
+    if (b >= hist_blocks(g, n_sel)) return;
+    const bool is_k = blockIdx.y == 0;
+    const long long Lh = (long long)n_sel * g.Tp;
+    const long long t0 = (long long)b * g.Binter;
+    const long long t1 = t0 + g.Binter < Lh ? t0 + g.Binter : Lh;
+    const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const int col0 = (slab * 32 + lane) * 8;
+    const T* src = is_k ? pool_k : pool_v;
+    T* dst = is_k ? k_hist : v_hist;
+    // slot of the block's first row; later rows step across page seams
+    const int slot0 = (int)(t0 / g.Tp);
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (col0 < g.HD) {
+        for (long long t = t0 + grp; t < t1; t += 8 * kRows) {
+            Row8<T> v[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                const long long tu = t + 8 * u;
+                if (tu < t1) {
+                    int slot = slot0;
+                    long long first = (long long)slot0 * g.Tp;
+                    while (tu - first >= g.Tp) { ++slot; first += g.Tp; }
+                    const long long srow = (long long)page_idx[slot] * g.Tp + (tu - first);
+                    v[u].load(src + srow * g.HD + col0);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                const long long tu = t + 8 * u;
+                if (tu < t1) {
+                    v[u].store(dst + tu * g.HD + col0);
+                    if (is_k) v[u].add_to(acc);
+                }
+            }
+        }
+    }
+    if (!is_k) return;
+    __shared__ float part[8][32 * 8 + 4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[grp][lane * 8 + e] = acc[e];
+    __syncthreads();
+    const int c = slab * 256 + threadIdx.x;
+    if (c < g.HD) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s += part[k][threadIdx.x];
+        const int h = c / g.d, e = c % g.d;
+        kb[((size_t)h * g.NB_max + b) * g.d + e] = s / (float)(t1 - t0);
+    }
+}
+
+template <typename T>
+void launch_gather_pool(const Geo& g, const void* pool_k, const void* pool_v, const int32_t* page_idx,
+                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, hipStream_t st) {
+    dim3 grid((unsigned)((long long)g.NBh_max * ((g.HD + 255) / 256)), 2);
+    hipLaunchKernelGGL(k_gather_pool<T>, grid, dim3(256), 0, st, g, (const T*)pool_k, (const T*)pool_v,
+                       page_idx, n_sel, (T*)k_hist, (T*)v_hist, kb);
+}
+template void launch_gather_pool<float>(const Geo&, const void*, const void*, const int32_t*, const int32_t*,
+                                        void*, void*, float*, hipStream_t);
+template void launch_gather_pool<bf16_t>(const Geo&, const void*, const void*, const int32_t*, const int32_t*,
+                                         void*, void*, float*, hipStream_t);
+
 void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* pool_v,
                    const int32_t* page_idx, const int32_t* n_sel, void* k_hist, void* v_hist,
                    hipStream_t st) {

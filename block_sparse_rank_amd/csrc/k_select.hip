@@ -12,16 +12,17 @@
 // key blocks and chunk key blocks. One work-group per (token block, 256
 // columns): 32 column lanes of 8 elements x 8 token groups, Kahan-free fixed
 // order sums (blocks are at most 512 tokens).
-//   blockIdx.x in [0, NQB)               : query block i       -> qb[h][i][:]
-//   blockIdx.x in [NQB, NQB + NBh_max)   : history block b     -> kb[h][b][:]
-//   blockIdx.x in [NQB + NBh_max, ...)   : chunk block j       -> kb[h][NBh + j][:]
+//   blockIdx.x in [0, NQB)                 : query block i    -> qb[h][i][:]
+//   blockIdx.x in [NQB, NQB + hist_grid)   : history block b  -> kb[h][b][:]
+//   blockIdx.x in [NQB + hist_grid, ...)   : chunk block j    -> kb[h][NBh + j][:]
+// hist_grid is NBh_max, or 0 when the gather has pooled the history blocks.
 // kb rows are indexed with the present history length, so chunk blocks
 // follow the last present history block directly.
 
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_pool(Geo g, const T* __restrict__ q, const T* __restrict__ k_hist, const T* __restrict__ k_intra,
-       const int32_t* __restrict__ n_sel_p, float* __restrict__ qb, float* __restrict__ kb) {
+       const int32_t* __restrict__ n_sel_p, float* __restrict__ qb, float* __restrict__ kb, int hist_grid) {
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
     const long long Lh = (long long)n_sel * g.Tp;
@@ -36,7 +37,7 @@ k_pool(Geo g, const T* __restrict__ q, const T* __restrict__ k_hist, const T* __
         t1 = t0 + g.Bq < g.Lq ? t0 + g.Bq : g.Lq;
         dst = qb + (size_t)bx * g.d;
         dst_head_stride = (size_t)g.NQB * g.d;
-    } else if (bx < g.NQB + g.NBh_max) {
+    } else if (bx < g.NQB + hist_grid) {
         int b = bx - g.NQB;
         if (b >= NBh) return;
         src = k_hist;
@@ -45,7 +46,7 @@ k_pool(Geo g, const T* __restrict__ q, const T* __restrict__ k_hist, const T* __
         dst = kb + (size_t)b * g.d;
         dst_head_stride = (size_t)g.NB_max * g.d;
     } else {
-        int j = bx - g.NQB - g.NBh_max;
+        int j = bx - g.NQB - hist_grid;
         src = k_intra;
         t0 = (long long)j * g.Bintra;
         t1 = t0 + g.Bintra < g.Lq ? t0 + g.Bintra : g.Lq;
@@ -92,15 +93,16 @@ k_pool(Geo g, const T* __restrict__ q, const T* __restrict__ k_hist, const T* __
 
 template <typename T>
 void launch_pool(const Geo& g, const void* q, const void* k_hist, const void* k_intra,
-                 const int32_t* n_sel, float* qb, float* kb, hipStream_t st) {
-    dim3 grid(g.NQB + g.NBh_max + g.NBc, (g.HD + 255) / 256);
+                 const int32_t* n_sel, float* qb, float* kb, bool hist_pooled, hipStream_t st) {
+    const int hist_grid = hist_pooled ? 0 : g.NBh_max;
+    dim3 grid(g.NQB + hist_grid + g.NBc, (g.HD + 255) / 256);
     hipLaunchKernelGGL(k_pool<T>, grid, dim3(256), 0, st, g, (const T*)q, (const T*)k_hist,
-                       (const T*)k_intra, n_sel, qb, kb);
+                       (const T*)k_intra, n_sel, qb, kb, hist_grid);
 }
 template void launch_pool<float>(const Geo&, const void*, const void*, const void*, const int32_t*,
-                                 float*, float*, hipStream_t);
+                                 float*, float*, bool, hipStream_t);
 template void launch_pool<bf16_t>(const Geo&, const void*, const void*, const void*,
-                                  const int32_t*, float*, float*, hipStream_t);
+                                  const int32_t*, float*, float*, bool, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Selection: one work-group (256 threads) per row (head h, query block i).

@@ -27,10 +27,15 @@ void launch_retrieve(const Geo&, const float* partial, const float* page_kmean, 
                      int cur_prompt, int32_t* page_idx, int32_t* n_sel, hipStream_t);
 void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* pool_v, const int32_t* page_idx,
                    const int32_t* n_sel, void* k_hist, void* v_hist, hipStream_t);
+// The gather with the history blocks of the pooled keys kb written on the way.
+template <typename T>
+void launch_gather_pool(const Geo&, const void* pool_k, const void* pool_v, const int32_t* page_idx,
+                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, hipStream_t);
 
+// hist_pooled: the history blocks of kb are already written (launch_gather_pool)
 template <typename T>
 void launch_pool(const Geo&, const void* q, const void* k_hist, const void* k_intra, const int32_t* n_sel,
-                 float* qb, float* kb, hipStream_t);
+                 float* qb, float* kb, bool hist_pooled, hipStream_t);
 void launch_select(const Geo&, const float* qb, const float* kb, float* zl, const int32_t* n_sel, const TauArg& tau,
                    int32_t* sel_count, int32_t* sel_idx, uint8_t* sel_mask, float* block_mass, hipStream_t);
 
