@@ -152,6 +152,41 @@ def test_forward_end_to_end(case):
     compare("out(fwd)", got[keep], ref["out"][keep], s.dtype)
 
 
+def test_forward_matches_stages(case):
+    """hsa_forward against the entry points called one after another on the same
+    inputs. The forward pools the history keys inside the gather and runs the
+    low-rank branch on a second stream; neither may change a result: pages,
+    gathered rows, selection and both branches agree bit for bit. The gate and
+    the gated output differ from hsa_fuse's by rounding only (the gate's dot
+    product is summed in another order)."""
+    s = case.s
+    km = case.page_summary()
+    f = case.forward(km)
+    page_idx, n_sel, k_hist, v_hist = case.gather(km)
+    n = int(host(n_sel)[0])
+    assert int(host(f["n_sel"])[0]) == n
+    assert host(f["page_idx"])[:n].tolist() == host(page_idx)[:n].tolist()
+    rows = n * s.Tp
+    assert host(f["k_hist"])[:rows].tobytes() == host(k_hist)[:rows].tobytes()
+    assert host(f["v_hist"])[:rows].tobytes() == host(v_hist)[:rows].tobytes()
+    cnt, idx, _, _ = case.select(k_hist, n_sel)
+    c, fi, si = host(cnt), host(f["sel_idx"]), host(idx)
+    assert np.array_equal(host(f["sel_count"]), c)
+    for h in range(s.H):
+        for i in range(c.shape[1]):
+            assert np.array_equal(fi[h, i, :c[h, i]], si[h, i, :c[h, i]]), (h, i)
+    o_s = case.sparse(k_hist, v_hist, n_sel, cnt, idx)
+    assert host(f["o_sparse"]).tobytes() == host(o_s).tobytes()
+    o_l, _, _ = case.linear(k_hist, v_hist, n_sel)
+    assert host(f["o_linear"]).tobytes() == host(o_l).tobytes()
+    out, gate = case.fuse(o_s, o_l)
+    g_f, g_s = host(f["gate"]), host(gate)
+    assert np.max(np.abs(g_f - g_s)) <= 1e-6
+    a, b = oracle.as_f64(host(f["out"]), s.dtype), oracle.as_f64(host(out), s.dtype)
+    ulp = 2.0 ** -7 if s.dtype == "bf16" else 2.0 ** -20
+    assert np.all(np.abs(a - b) <= ulp * np.abs(b) + 1e-6)
+
+
 def test_forward_is_deterministic(case):
     km = case.page_summary()
     a = host(case.forward(km)["out"])
