@@ -10,8 +10,8 @@
 // ---------------------------------------------------------------------------
 // Column sums over a run of token rows. Block = 64 column lanes x 4 token
 // groups; each thread keeps a Kahan sum over its token group, then the four
-// groups are added in a fixed order. Used for the page summary (one page per
-// blockIdx.x) and for the chunk-mean query (one token slab per blockIdx.x).
+// groups are added in a fixed order. Used for the chunk-mean query (one token
+// slab per blockIdx.x).
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -45,14 +45,6 @@ k_colsum(const T* __restrict__ x, long long rows_per_item, long long item_stride
     }
 }
 
-template <typename T>
-void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hipStream_t st) {
-    dim3 grid(g.P, (g.HD + 63) / 64);
-    hipLaunchKernelGGL(k_colsum<T>, grid, dim3(256), 0, st, (const T*)pool_k, (long long)g.Tp,
-                       (long long)g.Tp, 0, g.HD, 1.0f / (float)g.Tp, page_kmean, g.HD);
-}
-template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
-template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Retrieval, step 1: partial column sums of q over token slabs.
@@ -348,3 +340,58 @@ void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* 
     hipLaunchKernelGGL(k_gather, grid, dim3(kGatherThreads), 0, st, (const u32x4*)pool_k,
                        (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec);
 }
+
+// Page summary: one work-group of 1024 threads per (page, 256 columns): 32
+// column lanes of 8 elements x 32 row groups, 16 rows (bf16; 8 for f32) in
+// flight per thread as raw vectors. Each thread keeps a Kahan sum per column over its rows
+// (in row order); the 32 group sums are added in group order, again with
+// Kahan, so identical pages give identical means.
+template <typename T>
+__global__ void __launch_bounds__(1024)
+k_page_mean(const T* __restrict__ pool_k, int Tp, int HD, float inv_Tp, float* __restrict__ out) {
+    const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const int col0 = (blockIdx.y * 32 + lane) * 8;
+    const long long page = blockIdx.x;
+    const T* base = pool_k + page * (long long)Tp * HD + col0;
+    Kahan acc[8];
+    if (col0 < HD) {
+        constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
+        for (int t = grp; t < Tp; t += 32 * kRows) {
+            Row8<T> v[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                const int tu = t + 32 * u < Tp ? t + 32 * u : t;
+                v[u].load(base + (long long)tu * HD);
+            }
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                if (t + 32 * u < Tp) {
+                    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    v[u].add_to(x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e].add(x[e]);
+                }
+        }
+    }
+    __shared__ float part[32][32 * 8 + 4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[grp][lane * 8 + e] = acc[e].s;
+    __syncthreads();
+    if (threadIdx.x < 256) {
+        const int c = blockIdx.y * 256 + threadIdx.x;
+        if (c < HD) {
+            Kahan k;
+            for (int q = 0; q < 32; ++q) k.add(part[q][threadIdx.x]);
+            out[page * HD + c] = k.s * inv_Tp;
+        }
+    }
+}
+
+template <typename T>
+void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hipStream_t st) {
+    dim3 grid(g.P, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_page_mean<T>, grid, dim3(1024), 0, st, (const T*)pool_k, g.Tp, g.HD,
+                       1.0f / (float)g.Tp, page_kmean);
+}
+template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
+template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
