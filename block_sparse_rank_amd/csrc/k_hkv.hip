@@ -275,22 +275,16 @@ k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
     const int col0 = (slab * 32 + lane) * 8;
     const T* src = is_k ? pool_k : pool_v;
     T* dst = is_k ? k_hist : v_hist;
-    // slot of the block's first row; later rows step across page seams
-    const int slot0 = (int)(t0 / g.Tp);
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col0 < g.HD) {
+    // rows t, t + 8, ... of this thread's group, kRows loads in flight; row
+    // tu of the active history is row srow(tu) of the pool
+    auto copy_rows = [&](auto srow) __attribute__((always_inline)) {
         for (long long t = t0 + grp; t < t1; t += 8 * kRows) {
             Row8<T> v[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
                 const long long tu = t + 8 * u;
-                if (tu < t1) {
-                    int slot = slot0;
-                    long long first = (long long)slot0 * g.Tp;
-                    while (tu - first >= g.Tp) { ++slot; first += g.Tp; }
-                    const long long srow = (long long)page_idx[slot] * g.Tp + (tu - first);
-                    v[u].load(src + srow * g.HD + col0);
-                }
+                if (tu < t1) v[u].load(src + srow(tu) * g.HD + col0);
             }
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
@@ -300,6 +294,26 @@ k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
                     if (is_k) v[u].add_to(acc);
                 }
             }
+        }
+    };
+    if (col0 < g.HD) {
+        const int slot0 = (int)(t0 / g.Tp);
+        const long long first0 = (long long)slot0 * g.Tp;
+        if (g.Binter <= g.Tp) {
+            // the block touches the pages of slot0 and slot0 + 1 at most: both
+            // looked up once, so no row load waits for a page lookup
+            const long long pa = page_idx[slot0];
+            const long long pb = slot0 + 1 < n_sel ? page_idx[slot0 + 1] : pa;
+            copy_rows([&](long long tu) {
+                const long long rel = tu - first0;
+                return rel < g.Tp ? pa * g.Tp + rel : pb * g.Tp + (rel - g.Tp);
+            });
+        } else {
+            // short pages: several per block, each row looks its page up
+            copy_rows([&](long long tu) {
+                const long long slot = tu / g.Tp;
+                return (long long)page_idx[slot] * g.Tp + (tu - slot * g.Tp);
+            });
         }
     }
     if (!is_k) return;
