@@ -8,62 +8,14 @@
 #include "launch.h"
 
 // ---------------------------------------------------------------------------
-// Column sums over a run of token rows. Block = 64 column lanes x 4 token
-// groups; each thread keeps a Kahan sum over its token group, then the four
-// groups are added in a fixed order. Used for the chunk-mean query (one token
-// slab per blockIdx.x).
-
-template <typename T>
-__global__ void __launch_bounds__(256)
-k_colsum(const T* __restrict__ x, long long rows_per_item, long long item_stride_rows,
-         int rows_per_slab, int HD, float scale, float* __restrict__ out, int out_stride) {
-    const int lane = threadIdx.x & 63;
-    const int grp = threadIdx.x >> 6;
-    const int col = blockIdx.y * 64 + lane;
-    const long long item = blockIdx.x;
-    // rows [r0, r1) of this block
-    long long r0, r1;
-    if (rows_per_slab > 0) {          // slabs of one long run
-        r0 = item * rows_per_slab;
-        r1 = r0 + rows_per_slab;
-        if (r1 > rows_per_item) r1 = rows_per_item;
-    } else {                          // one whole item (a page)
-        r0 = 0;
-        r1 = rows_per_item;
-    }
-    const T* base = x + (rows_per_slab > 0 ? 0 : item * item_stride_rows * HD);
-    Kahan acc;
-    if (col < HD) {
-        for (long long t = r0 + grp; t < r1; t += 4) acc.add(Elt<T>::to_f32(base[t * HD + col]));
-    }
-    __shared__ float part[4][64];
-    part[grp][lane] = acc.s;
-    __syncthreads();
-    if (grp == 0 && col < HD) {
-        float s = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
-        out[item * out_stride + col] = s * scale;
-    }
-}
-
-
-// ---------------------------------------------------------------------------
-// Retrieval, step 1: partial column sums of q over token slabs.
+// Retrieval, step 1: partial column sums of q over token slabs (k_item_colsum,
+// below).
 
 int retrieve_slabs(const Geo& g) {
     int slabs = (g.Lq + 63) / 64;
     return slabs > 64 ? 64 : slabs;
 }
 
-template <typename T>
-void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
-    int slabs = retrieve_slabs(g);
-    int per = (g.Lq + slabs - 1) / slabs;
-    dim3 grid(slabs, (g.HD + 63) / 64);
-    hipLaunchKernelGGL(k_colsum<T>, grid, dim3(256), 0, st, (const T*)q, (long long)g.Lq, 0LL, per,
-                       g.HD, 1.0f, partial, g.HD);
-}
-template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
-template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Retrieval, step 2: chunk-mean query, one column per thread, slab partials
@@ -96,7 +48,6 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
     float* qbar = smem;                       // [HD]
     float* score = smem + HD;                 // [P]
     int* cand = reinterpret_cast<int*>(score + P);      // [P] 1 if the page matches
-    int* by_rank = cand + P;                  // [64]
     __shared__ int n_cand;
 
     const int tid = threadIdx.x;
@@ -106,17 +57,23 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
 
     for (int c = tid; c < HD; c += kRetrieveThreads) qbar[c] = qbar_g[c];
     if (tid == 0) n_cand = 0;
-    if (tid < 64) by_rank[tid] = -1;
     __syncthreads();
 
     // page scores, one wave per page; lanes take columns lane, lane + 64, ...
-    // in a fixed order (eight independent loads in flight), then a fixed tree
+    // in a fixed order (up to 24 independent loads in flight), then a fixed tree
     for (int p = wave; p < P; p += nwaves) {
         const bool match = page_prompt[p] == cur_prompt;
         float s = 0.f;
         if (match) {
             const float* km = page_kmean + (size_t)p * HD;
             int c = lane;
+            for (; c + 23 * 64 < HD; c += 24 * 64) {   // 24 loads in flight (one pass at H d = 1536)
+                float k24[24];
+#pragma unroll
+                for (int u = 0; u < 24; ++u) k24[u] = km[c + 64 * u];
+#pragma unroll
+                for (int u = 0; u < 24; ++u) s = fmaf(k24[u], qbar[c + 64 * u], s);
+            }
             for (; c + 7 * 64 < HD; c += 8 * 64) {
                 float k8[8];
 #pragma unroll
@@ -135,7 +92,9 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
     }
     __syncthreads();
 
-    // rank of each candidate: better score, or equal score and lower index
+    // rank of each candidate: better score, or equal score and lower index;
+    // the Kp best are marked chosen (cand = 2; still nonzero for the others'
+    // candidate test)
     for (int p = tid; p < P; p += kRetrieveThreads) {
         if (!cand[p]) continue;
         const float sp = score[p];
@@ -145,26 +104,25 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
             const float so = score[o];
             if (so > sp || (so == sp && o < p)) ++rank;
         }
-        if (rank < Kp) by_rank[rank] = p;
+        if (rank < Kp) cand[p] = 2;
     }
     __syncthreads();
 
-    if (tid == 0) {
-        int n = n_cand < Kp ? n_cand : Kp;
-        int chosen[64];
-        for (int k = 0; k < n; ++k) chosen[k] = by_rank[k];
-        for (int a = 1; a < n; ++a) {            // insertion sort, ascending page index
-            int v = chosen[a], b = a - 1;
-            while (b >= 0 && chosen[b] > v) { chosen[b + 1] = chosen[b]; --b; }
-            chosen[b + 1] = v;
-        }
-        for (int k = 0; k < Kp; ++k) page_idx[k] = k < n ? chosen[k] : -1;
-        *n_sel = n;
+    // slots in ascending page order: a chosen page's slot is the number of
+    // chosen pages below it
+    const int n = n_cand < Kp ? n_cand : Kp;
+    for (int p = tid; p < P; p += kRetrieveThreads) {
+        if (cand[p] != 2) continue;
+        int slot = 0;
+        for (int o = 0; o < p; ++o) slot += cand[o] == 2 ? 1 : 0;
+        page_idx[slot] = p;
     }
+    for (int k = n + tid; k < Kp; k += kRetrieveThreads) page_idx[k] = -1;
+    if (tid == 0) *n_sel = n;
 }
 
 size_t retrieve_smem_bytes(const Geo& g) {
-    return (size_t)g.HD * 4 + (size_t)g.P * 8 + 64 * 4;
+    return (size_t)g.HD * 4 + (size_t)g.P * 8;
 }
 
 void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
@@ -355,35 +313,42 @@ void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* 
                        (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec);
 }
 
-// Page summary: one work-group of 1024 threads per (page, 256 columns): 32
-// column lanes of 8 elements x 32 row groups, 16 rows (bf16; 8 for f32) in
-// flight per thread as raw vectors. Each thread keeps a Kahan sum per column over its rows
-// (in row order); the 32 group sums are added in group order, again with
-// Kahan, so identical pages give identical means.
+// Column sums of items of consecutive token rows: item i is rows
+// [i n, min((i + 1) n, total)) of x, its sum (times `scale`) goes to out[i].
+// Used for the page summary (items = pages, scale 1/Tp) and for the slab sums
+// of the chunk-mean query. One work-group of 1024 threads per (item, 256
+// columns): 32 column lanes of 8 elements x 32 row groups, 16 rows (bf16; 8
+// for f32) in flight per thread as raw vectors. Each thread keeps a Kahan
+// sum per column over its rows (in row order); the 32 group sums are added
+// in group order, again with Kahan, so identical items give identical sums.
 template <typename T>
 __global__ void __launch_bounds__(1024)
-k_page_mean(const T* __restrict__ pool_k, int Tp, int HD, float inv_Tp, float* __restrict__ out) {
+k_item_colsum(const T* __restrict__ x, long long rows_per_item, long long total_rows, int HD, float scale,
+              float* __restrict__ out) {
     const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
     const int col0 = (blockIdx.y * 32 + lane) * 8;
-    const long long page = blockIdx.x;
-    const T* base = pool_k + page * (long long)Tp * HD + col0;
+    const long long item = blockIdx.x;
+    const long long r0 = item * rows_per_item;
+    const long long left = total_rows - r0;
+    const int rows = (int)(left < rows_per_item ? left : rows_per_item);
+    const T* base = x + r0 * HD + col0;
     Kahan acc[8];
     if (col0 < HD) {
         constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
-        for (int t = grp; t < Tp; t += 32 * kRows) {
+        for (int t = grp; t < rows; t += 32 * kRows) {
             Row8<T> v[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
-                const int tu = t + 32 * u < Tp ? t + 32 * u : t;
+                const int tu = t + 32 * u < rows ? t + 32 * u : t;
                 v[u].load(base + (long long)tu * HD);
             }
 #pragma unroll
             for (int u = 0; u < kRows; ++u)
-                if (t + 32 * u < Tp) {
-                    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    v[u].add_to(x);
+                if (t + 32 * u < rows) {
+                    float xv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    v[u].add_to(xv);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e].add(x[e]);
+                    for (int e = 0; e < 8; ++e) acc[e].add(xv[e]);
                 }
         }
     }
@@ -396,7 +361,7 @@ k_page_mean(const T* __restrict__ pool_k, int Tp, int HD, float inv_Tp, float* _
         if (c < HD) {
             Kahan k;
             for (int q = 0; q < 32; ++q) k.add(part[q][threadIdx.x]);
-            out[page * HD + c] = k.s * inv_Tp;
+            out[item * HD + c] = k.s * scale;
         }
     }
 }
@@ -404,8 +369,19 @@ k_page_mean(const T* __restrict__ pool_k, int Tp, int HD, float inv_Tp, float* _
 template <typename T>
 void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hipStream_t st) {
     dim3 grid(g.P, (g.HD + 255) / 256);
-    hipLaunchKernelGGL(k_page_mean<T>, grid, dim3(1024), 0, st, (const T*)pool_k, g.Tp, g.HD,
-                       1.0f / (float)g.Tp, page_kmean);
+    hipLaunchKernelGGL(k_item_colsum<T>, grid, dim3(1024), 0, st, (const T*)pool_k, (long long)g.Tp,
+                       (long long)g.P * g.Tp, g.HD, 1.0f / (float)g.Tp, page_kmean);
 }
 template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
 template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
+
+template <typename T>
+void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
+    const int slabs = retrieve_slabs(g);
+    const int per = (g.Lq + slabs - 1) / slabs;
+    dim3 grid(slabs, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_item_colsum<T>, grid, dim3(1024), 0, st, (const T*)q, (long long)per, (long long)g.Lq,
+                       g.HD, 1.0f, partial);
+}
+template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
+template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
