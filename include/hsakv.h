@@ -234,7 +234,13 @@ int hsa_fuse(const hsakv_dims* dims, const void* q, const float* w_g, const floa
  * sparse attention and the gate, with the gate fused into the sparse
  * attention's epilogue. Results equal the separate entry points run in that
  * order. tau (host, H floats) and cur_prompt (host) as above. Workspace:
- * HSAKV_ENTRY_FORWARD. */
+ * HSAKV_ENTRY_FORWARD.
+ * For bf16 the low-rank branch runs on a second, library-owned stream of
+ * the current device (one per device, default priority), forked from
+ * `stream` after the gather and joined back into it with events before the
+ * attention, so all of the call's work is still ordered on `stream`. Calls
+ * from several host threads on one device share that stream: they stay
+ * correct but serialise their low-rank branches. */
 int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
                 const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
                 void* stream);
