@@ -150,27 +150,50 @@ k_lowrank_proj(Geo g, const T* __restrict__ E, const T* __restrict__ F,
 }
 
 // Sum the split partials in split order; write K', V' (f32, optional) and
-// the attention operands: bf16 hi + lo pair, or the f32 values.
+// the attention operands: bf16 hi + lo pair, or the f32 values. Four
+// consecutive elements per thread (r H d is a multiple of 64), eight split
+// loads in flight; the sums still run in split order.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_lowrank_reduce(int nsplit, long long n_per_z, const float* __restrict__ part,
                  float* __restrict__ k_low, float* __restrict__ v_low, T* __restrict__ k_hi,
                  T* __restrict__ v_hi, T* __restrict__ k_lo, T* __restrict__ v_lo) {
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (idx >= 2 * n_per_z) return;
     const int z = idx >= n_per_z;
     const long long e = idx - z * n_per_z;
-    float s = 0.f;
-    for (int k = 0; k < nsplit; ++k) s += part[((long long)(k * 2 + z)) * n_per_z + e];
+    const float* src = part + (long long)z * n_per_z + e;
+    const long long stride = 2 * n_per_z;   // next split, same z
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nsplit; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < nsplit) v[u] = *reinterpret_cast<const float4*>(src + (long long)(k0 + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < nsplit) {
+                s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+            }
+    }
     float* low = z ? v_low : k_low;
-    if (low) low[e] = s;
+    if (low) *reinterpret_cast<float4*>(low + e) = s;
     T* hi = z ? v_hi : k_hi;
     if constexpr (sizeof(T) == 2) {
-        const bf16_t h = f32_to_bf16(s);
-        hi[e] = h;
-        (z ? v_lo : k_lo)[e] = f32_to_bf16(s - bf16_to_f32(h));
+        const float sv[4] = {s.x, s.y, s.z, s.w};
+        bf16_t h[4], l[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            h[c] = f32_to_bf16(sv[c]);
+            l[c] = f32_to_bf16(sv[c] - bf16_to_f32(h[c]));
+        }
+        uint2 ph, pl;
+        ph.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16); ph.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        pl.x = (uint32_t)l[0] | ((uint32_t)l[1] << 16); pl.y = (uint32_t)l[2] | ((uint32_t)l[3] << 16);
+        *reinterpret_cast<uint2*>(hi + e) = ph;
+        *reinterpret_cast<uint2*>((z ? v_lo : k_lo) + e) = pl;
     } else {
-        hi[e] = s;
+        *reinterpret_cast<float4*>(hi + e) = s;
     }
 }
 
@@ -229,7 +252,7 @@ template <typename T>
 void launch_lowrank_reduce(const Geo& g, const float* part, float* k_low, float* v_low, void* k_hi,
                            void* v_hi, void* k_lo, void* v_lo, hipStream_t st) {
     const long long n = (long long)g.r * g.HD;
-    const long long blocks = (2 * n + 255) / 256;
+    const long long blocks = (2 * n / 4 + 255) / 256;   // four elements per thread
     hipLaunchKernelGGL(k_lowrank_reduce<T>, dim3((unsigned)blocks), dim3(256), 0, st,
                        lowrank_splits(g), n, part, k_low, v_low, (T*)k_hi, (T*)v_hi, (T*)k_lo,
                        (T*)v_lo);
