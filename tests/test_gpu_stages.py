@@ -49,6 +49,12 @@ VARIANTS = [
     # six k-steps per split (the LDS ring wraps), a split across the seam
     ("bf16-r128-long", _variant("tiny", dtype="bf16", H=2, d=128, r=128, Lq=1000, tokens_per_frame=100,
                                 clustered=True, tau_law="uniform", seed=27), {}),
+    # eight slots out of 24 pages: the retrieval's slot order over more chosen pages
+    ("kp8-p24", _variant("tiny", Kp=8, P=24, seed=28), {}),
+    # 160-token pages: 128-row history blocks straddle page seams while no block
+    # spans more than two pages (the gather's two-page path)
+    ("bf16-tp160", _variant("tiny", dtype="bf16", tokens_per_frame=20, Kp=3, P=6, clustered=True,
+                            tau_law="uniform", seed=29), {}),
 ]
 
 
