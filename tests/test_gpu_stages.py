@@ -193,6 +193,15 @@ def test_forward_matches_stages(case):
     assert np.all(np.abs(a - b) <= ulp * np.abs(b) + 1e-6)
 
 
+def test_forward_with_only_out(case):
+    """With only `out` requested every intermediate lives in the workspace (as
+    in the bench): the output is the same, bit for bit, as with all outputs."""
+    km = case.page_summary()
+    full = host(case.forward(km)["out"])
+    bare = host(case.forward(km, debug=False)["out"])
+    assert full.tobytes() == bare.tobytes()
+
+
 def test_forward_is_deterministic(case):
     km = case.page_summary()
     a = host(case.forward(km)["out"])
