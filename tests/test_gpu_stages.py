@@ -209,6 +209,37 @@ def test_forward_is_deterministic(case):
     assert a.tobytes() == b.tobytes()
 
 
+def test_forward_from_two_threads():
+    """bf16 forwards from two host threads, each on its own stream and
+    workspace, share the library's second stream: every result equals the
+    one-thread result bit for bit."""
+    import threading
+    s = _variant("tiny", dtype="bf16", clustered=True, tau_law="uniform", seed=30)
+    c = Case(s)
+    km = c.page_summary()
+    ref = host(c.forward(km, debug=False)["out"]).tobytes()
+    torch.cuda.synchronize()
+    results, errors = [], []
+
+    def worker():
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                outs = [c.forward(km, debug=False)["out"] for _ in range(3)]
+            st.synchronize()
+            results.extend(host(o).tobytes() for o in outs)
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert len(results) == 6 and all(r == ref for r in results)
+
+
 # ---------------------------------------------------------------------------
 # special cases with closed forms on the GPU
 
