@@ -95,27 +95,42 @@ def main() -> int:
     outs = {"out": out, "sel_count": sel_count, "sel_idx": sel_idx, "n_sel": n_sel}
     tau = ch["tau"]
     stream = torch.cuda.current_stream()
+    fork = hs.fork_create()          # the caller-owned second stream of the forward
 
     def step():
-        hs.hsa_forward(d, tau, s.cur_prompt, ins, outs, ws_fwd, stream=stream)
+        hs.hsa_forward(d, tau, s.cur_prompt, ins, outs, ws_fwd, stream=stream, fork=fork)
 
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
+
+    # headline: each step timed alone by HIP events on the launch stream, with
+    # 1 GiB written before it (outside the events) so that no input or
+    # intermediate is left in the 256 MB MALL or the L2 caches
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(a.steps):
+    for k in range(a.steps):
+        flush.fill_(k & 0xff)
+        evs[k][0].record(stream)
         step()
+        evs[k][1].record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / a.steps
+    cold = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ms_med, ms_p10, ms_p90 = (float(np.percentile(cold, q)) for q in (50, 10, 90))
 
-    # the same steps bracketed by HIP events on the launch stream
+    # secondary: the same steps back to back (warm caches), mean per step
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(a.steps):
         step()
     ev[1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = ev[0].elapsed_time(ev[1]) / a.steps
+    warm_ms = ev[0].elapsed_time(ev[1]) / a.steps
+    del flush
 
     # selection actually taken: algorithmic work of the sparse attention
     n = int(n_sel.cpu()[0])
@@ -137,15 +152,16 @@ def main() -> int:
     sparse_flops = 4.0 * s.d * pairs                        # QK^T and PV, 2 flops per MAC
     eb = 2 if s.dtype == "bf16" else 4
     gather_bytes = 2.0 * 2 * n * s.Tp * s.H * s.d * eb       # K and V, read + write
+    floor_us, floor_parts = forward_floor(s, n, sparse_flops)
 
     result = {
         "metric": "HSA fwd ms per chunk-layer (1.3B-shape 480p, Kp=4) + % HBM/MFMA roofline",
-        "value": round(ms_per_step, 4),
+        "value": round(ms_med, 4),
         "unit": "ms",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(ms_med, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -155,7 +171,16 @@ def main() -> int:
                    "Kp": s.Kp, "r": s.r, "Binter": s.Binter, "Bintra": s.Bintra, "Bq": s.Bq,
                    "tau_min": s.tau_min, "selected_block_density": round(density, 4),
                    "parallelism": "single-gpu"},
-        "wall_ms_per_step": round(wall_ms, 4),
+        "timing": {"headline": "median of per-step HIP-event times, 1 GiB written before each step "
+                               "(cold MALL and L2)",
+                   "median_ms": round(ms_med, 4), "p10_ms": round(ms_p10, 4),
+                   "p90_ms": round(ms_p90, 4), "warm_mean_ms": round(warm_ms, 4),
+                   "wall_ms_per_step_incl_flush": round(wall_ms, 4)},
+        "forward_roofline": {"floor_us": round(floor_us, 1),
+                             "frac": round(floor_us * 1e-3 / ms_med, 4),
+                             "floor_parts_us": {k: round(v, 1) for k, v in floor_parts.items()},
+                             "basis": "sum over stages of max(algorithmic bytes / 8 TB/s, "
+                                      "algorithmic flops / dense peak) at the measured selection"},
     }
 
     if not a.no_stages:
@@ -164,8 +189,33 @@ def main() -> int:
 
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, ch, pool_k, pool_v, a.cpu_budget)
+        result["cpu_baseline"]["ratio_to_gpu"] = round(result["cpu_baseline"]["value"] / ms_med, 1)
+    hs.fork_destroy(fork)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def forward_floor(s, n_sel, sparse_flops):
+    """Lower bound of one chunk-layer on this chip, in microseconds: per stage
+    the larger of its algorithmic HBM bytes at 8 TB/s and its algorithmic
+    flops at the dense peak of the storage type, summed over the stages."""
+    eb = 2 if s.dtype == "bf16" else 4
+    peak = (PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
+    bw = PEAK_HBM_GBS * 1e9
+    Lh = n_sel * s.Tp
+    tok = s.H * s.d * eb                      # bytes of one token row of one tensor
+    L_act = Lh + s.Lq
+    parts = {
+        "retrieve": s.Lq * tok / bw,                                    # read q
+        "gather": 4.0 * Lh * tok / bw,                                  # K and V, read + write
+        "select": (L_act + s.Lq) * tok / bw,                            # read K_act and q
+        "sparse_attn": sparse_flops / peak,
+        "linear": max((2 * s.r * L_act * eb + 2 * L_act * tok + s.Lq * tok + s.Lq * s.H * s.d * 4) / bw,
+                      (4.0 * s.r * L_act * s.H * s.d + 4.0 * s.Lq * s.r * s.H * s.d) / peak),
+        "fuse": (2 * s.Lq * s.H * s.d * 4 + 2 * s.Lq * tok) / bw,     # o_s, o_l in; q in, out
+    }
+    parts = {k: v * 1e6 for k, v in parts.items()}
+    return sum(parts.values()), parts
 
 
 def stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops, gather_bytes):
@@ -277,11 +327,24 @@ def cpu_baseline(s, ch, pool_k, pool_v, budget_s):
     metadata and is excluded.
     """
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     km = np.stack([oracle.page_summary(oracle.as_f64(pool_k[p], s.dtype)[None])[0]
                    for p in range(s.P)])
     t0 = time.perf_counter()
@@ -318,7 +381,8 @@ def cpu_baseline(s, ch, pool_k, pool_v, budget_s):
             "sample": (f"oracle O2-O13 in full for all {s.H} heads ({t_dense:.1f} s) + sparse "
                        f"attention on {n_rows} of {s.H * NQB} random rows ({t_sparse:.1f} s), "
                        f"scaled by selected (query, key) pairs {sample_pairs} -> {total_pairs}"),
-            "measured_s": round(t_dense + t_sparse, 1)}
+            "measured_s": round(t_dense + t_sparse, 1), "cpu_model": cpu_model, "blas": blas,
+            "ratio_to_gpu": None}
 
 
 if __name__ == "__main__":

@@ -5,12 +5,28 @@
 #include <math.h>
 #include <string.h>
 
-#include <mutex>
+#include <atomic>
 
 #include "common.h"
 #include "launch.h"
 
 #define HSAKV_API extern "C" __attribute__((visibility("default")))
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];   // zero-initialised: not looked up yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+    if (dev >= 0) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (dev >= 0) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 namespace {
 
@@ -65,6 +81,8 @@ int check_dims(const hsakv_dims* d) {
     // one-dimensional grids of (block, 256 columns) work-groups stay below 2^32 threads
     if ((long long)(g.NQB + g.NB_max) * ((g.HD + 255) / 256) * 256 >= (1LL << 32)) return HSAKV_ERR_UNSUPPORTED;
     if (retrieve_smem_bytes(g) > 65536) return HSAKV_ERR_UNSUPPORTED;
+    // the projection kernels address E and F with 32-bit byte offsets
+    if ((long long)d->r * g.L * g.elt >= (1LL << 31)) return HSAKV_ERR_UNSUPPORTED;
     return HSAKV_OK;
 }
 
@@ -86,19 +104,6 @@ int done() {
     return HSAKV_OK;
 }
 
-// A second stream per device (default priority, created on first use and
-// kept until the process ends) for work that can run beside the caller's
-// stream. nullptr if it cannot be created: the caller then stays on its own
-// stream.
-hipStream_t side_stream() {
-    static std::mutex mu;
-    static hipStream_t tab[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!tab[dev] && hipStreamCreateWithFlags(&tab[dev], hipStreamNonBlocking) != hipSuccess) tab[dev] = nullptr;
-    return tab[dev];
-}
 
 // ---- workspace sizes -------------------------------------------------------
 
@@ -165,23 +170,35 @@ void run_select(const Geo& g, const void* q, const void* k_hist, const void* k_i
     launch_select(g, qb, kb, zl, n_sel, tau, sel_count, sel_idx, sel_mask, block_mass, st);
 }
 
+// Scratch of the low-rank branch: split partials, then K' and V' (bf16 hi + lo
+// pairs, or float32).
+struct LinBufs {
+    float* part;
+    void *khi, *vhi, *klo, *vlo;
+};
+
+LinBufs carve_linear(const Geo& g, int eb, Carver& c) {
+    const size_t n = (size_t)g.r * g.HD;
+    LinBufs b;
+    b.part = (float*)c.take((size_t)lowrank_splits(g) * 2 * n * 4);
+    b.klo = b.vlo = nullptr;
+    if (eb == 2) {
+        b.khi = c.take(n * 2); b.vhi = c.take(n * 2); b.klo = c.take(n * 2); b.vlo = c.take(n * 2);
+    } else {
+        b.khi = c.take(n * 4); b.vhi = c.take(n * 4);
+    }
+    return b;
+}
+
 template <typename T>
 void run_linear(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
                 const void* k_intra, const void* v_intra, const int32_t* n_sel, const void* E,
-                const void* F, float* o_linear, float* k_low, float* v_low, Carver& c,
+                const void* F, float* o_linear, float* k_low, float* v_low, const LinBufs& b,
                 hipStream_t st) {
-    const size_t n = (size_t)g.r * g.HD;
-    float* part = (float*)c.take((size_t)lowrank_splits(g) * 2 * n * 4);
-    void *khi, *vhi, *klo = nullptr, *vlo = nullptr;
-    if (sizeof(T) == 2) {
-        khi = c.take(n * 2); vhi = c.take(n * 2); klo = c.take(n * 2); vlo = c.take(n * 2);
-    } else {
-        khi = c.take(n * 4); vhi = c.take(n * 4);
-    }
-    launch_lowrank_proj<T>(g, E, F, k_hist, v_hist, k_intra, v_intra, n_sel, part, st);
-    launch_lowrank_reduce<T>(g, part, k_low, v_low, khi, vhi, klo, vlo, st);
+    launch_lowrank_proj<T>(g, E, F, k_hist, v_hist, k_intra, v_intra, n_sel, b.part, st);
+    launch_lowrank_reduce<T>(g, b.part, k_low, v_low, b.khi, b.vhi, b.klo, b.vlo, st);
     Epi ep{o_linear, nullptr, nullptr, nullptr, nullptr, nullptr};
-    launch_lowrank_attn<T>(g, q, khi, vhi, klo, vlo, ep, st);
+    launch_lowrank_attn<T>(g, q, b.khi, b.vhi, b.klo, b.vlo, ep, st);
 }
 
 TauArg pack_tau(const hsakv_dims* d, const float* tau) {
@@ -300,6 +317,7 @@ HSAKV_API int hsa_select(const hsakv_dims* dims, const void* q, const void* k_hi
     float* qb = (float*)c.take((size_t)g.H * g.NQB * g.d * 4);
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
     float* zl = (float*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
+    if (!c.ok) return HSAKV_ERR_WORKSPACE;
     const TauArg t = pack_tau(dims, tau);
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
@@ -353,13 +371,15 @@ HSAKV_API int hsa_linear_branch(const hsakv_dims* dims, const void* q, const voi
     const int eb = elt_bytes(dims);
     HSAKV_CHECK(check_ws(ws, ws_bytes, ws_linear(g, eb)));
     Carver c{(char*)ws, ws_bytes};
+    const LinBufs lb = carve_linear(g, eb, c);
+    if (!c.ok) return HSAKV_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
     if (eb == 2)
         run_linear<bf16_t>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, E, F, o_linear, k_low,
-                           v_low, c, st);
+                           v_low, lb, st);
     else
         run_linear<float>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, E, F, o_linear, k_low,
-                          v_low, c, st);
+                          v_low, lb, st);
     return done();
 }
 
@@ -380,9 +400,43 @@ HSAKV_API int hsa_fuse(const hsakv_dims* dims, const void* q, const float* w_g, 
     return done();
 }
 
+HSAKV_API int hsakv_fork_create(hsakv_fork* f) {
+    if (!f) return HSAKV_ERR_NULL_ARG;
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        if (b) (void)hipEventDestroy(b);
+        if (a) (void)hipEventDestroy(a);
+        if (st) (void)hipStreamDestroy(st);
+        g_last_hip_error = (int)e;
+        return HSAKV_ERR_HIP;
+    }
+    f->stream = st;
+    f->fork = a;
+    f->join = b;
+    return HSAKV_OK;
+}
+
+HSAKV_API int hsakv_fork_destroy(hsakv_fork* f) {
+    if (!f) return HSAKV_ERR_NULL_ARG;
+    hipError_t e = hipSuccess, x;
+    if (f->join && (x = hipEventDestroy((hipEvent_t)f->join)) != hipSuccess) e = x;
+    if (f->fork && (x = hipEventDestroy((hipEvent_t)f->fork)) != hipSuccess) e = x;
+    if (f->stream && (x = hipStreamDestroy((hipStream_t)f->stream)) != hipSuccess) e = x;
+    f->stream = f->fork = f->join = nullptr;
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return HSAKV_ERR_HIP;
+    }
+    return HSAKV_OK;
+}
+
 HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
                           const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
-                          void* stream) {
+                          void* stream, const hsakv_fork* fork) {
     HSAKV_CHECK(check_dims(dims));
     HSAKV_REQUIRE(in && out, HSAKV_ERR_NULL_ARG);
     HSAKV_CHECK(check_tau(dims, tau));
@@ -390,6 +444,8 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
                       in->page_kmean && in->page_prompt && in->E && in->F && in->w_g && in->b_g &&
                       out->out,
                   HSAKV_ERR_NULL_ARG);
+    const bool split = fork && fork->stream;
+    HSAKV_REQUIRE(!split || (fork->fork && fork->join), HSAKV_ERR_NULL_ARG);
     HSAKV_REQUIRE(aligned(in->q) && aligned(in->k_intra) && aligned(in->v_intra) &&
                       aligned(in->pool_k) && aligned(in->pool_v) && aligned(in->page_kmean) &&
                       aligned(in->page_prompt, 4) && aligned(in->E) && aligned(in->F) &&
@@ -408,6 +464,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
     float* zl = (float*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
     void* sparse_ws = c.take(ws_sparse(g));
+    const LinBufs lb = carve_linear(g, eb, c);
     int32_t* page_idx = (int32_t*)c.take((size_t)g.Kp * 4);
     int32_t* n_sel = (int32_t*)c.take(4);
     void* k_hist = c.take((size_t)g.hist_rows * g.HD * eb);
@@ -415,6 +472,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     int32_t* sel_count = (int32_t*)c.take((size_t)g.H * g.NQB * 4);
     int32_t* sel_idx = (int32_t*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
     float* o_linear = (float*)c.take((size_t)g.Lq * g.HD * 4);
+    if (!c.ok) return HSAKV_ERR_WORKSPACE;   // every check is done before the first launch
     if (out->page_idx) page_idx = out->page_idx;
     if (out->n_sel) n_sel = out->n_sel;
     if (out->k_hist) k_hist = out->k_hist;
@@ -428,36 +486,49 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     if (eb == 2) {
         run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
-        // The low-rank branch needs the gathered KV only: it runs on a side
-        // stream beside the pooling, the block selection and the sparse plan
-        // (small, latency-bound kernels), and the attention waits for both.
-        hipStream_t side = side_stream();
-        hipEvent_t fork = nullptr, join = nullptr;
-        const bool split = side && side != st &&
-                           hipEventCreateWithFlags(&fork, hipEventDisableTiming) == hipSuccess &&
-                           hipEventCreateWithFlags(&join, hipEventDisableTiming) == hipSuccess &&
-                           hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
+        // The low-rank branch needs the gathered KV only: with a fork it runs
+        // on the caller's second stream beside the pooling, the block
+        // selection and the sparse plan (small, latency-bound kernels), and
+        // the attention waits for both.
+        hipStream_t side = split ? (hipStream_t)fork->stream : st;
+        if (split) {
+            hipError_t e = hipEventRecord((hipEvent_t)fork->fork, st);
+            if (e == hipSuccess) e = hipStreamWaitEvent(side, (hipEvent_t)fork->fork, 0);
+            if (e != hipSuccess) {
+                g_last_hip_error = (int)e;
+                return HSAKV_ERR_HIP;
+            }
+        }
         run_linear<bf16_t>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
-                           in->F, o_linear, nullptr, nullptr, c, split ? side : st);
-        const bool joined = split && hipEventRecord(join, side) == hipSuccess;
+                           in->F, o_linear, nullptr, nullptr, lb, side);
+        if (split) {
+            hipError_t e = hipEventRecord((hipEvent_t)fork->join, side);
+            if (e != hipSuccess) {
+                g_last_hip_error = (int)e;
+                return HSAKV_ERR_HIP;
+            }
+        }
         run_select<bf16_t>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                            nullptr, qb, kb, zl, true, st);
         launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, sparse_ws, st);
-        if (joined) (void)hipStreamWaitEvent(st, join, 0);
-        else if (split) (void)hipStreamSynchronize(side);   // branch enqueued but not joined: finish it
+        if (split) {
+            const hipError_t e = hipStreamWaitEvent(st, (hipEvent_t)fork->join, 0);
+            if (e != hipSuccess) {
+                g_last_hip_error = (int)e;
+                return HSAKV_ERR_HIP;
+            }
+        }
         launch_sparse_compute_bf16(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, sparse_ws, ep,
                                    st);
-        if (fork) (void)hipEventDestroy(fork);
-        if (join) (void)hipEventDestroy(join);
     } else {
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                           nullptr, qb, kb, zl, true, st);
         run_linear<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,
-                          in->F, o_linear, nullptr, nullptr, c, st);
+                          in->F, o_linear, nullptr, nullptr, lb, st);
         launch_sparse_attn<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,
                                   sel_count, sel_idx, sparse_ws, ep, st);
     }
-    return c.ok ? done() : HSAKV_ERR_WORKSPACE;
+    return done();
 }

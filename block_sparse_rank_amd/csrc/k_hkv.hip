@@ -83,6 +83,10 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
             }
             for (; c < HD; c += 64) s = fmaf(km[c], qbar[c], s);
             s = wave_sum(s);
+            // a score that is not a number ranks below every number: with
+            // -inf the rank test below is a total order (ties to the lower
+            // page), so exactly min(Kp, candidates) pages are chosen
+            if (__builtin_isnan(s)) s = -INFINITY;
         }
         if (lane == 0) {
             score[p] = s;

@@ -499,15 +499,6 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
             }
 }
 
-// CUs of the current device (cached per device).
-int device_cus() {
-    static int cache[64] = {0};
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-    if (dev >= 0 && dev < 64) cache[dev] = cus;
-    return cus;
-}
 
 bool big_tiles(const Geo& g) { return g.r >= 128 && g.HD % WN == 0; }
 
@@ -523,7 +514,7 @@ bool proj32_eligible(const Geo& g) {
 // with 128 x 128 tiles, one with 256 x 256) and no more, so no work-group
 // waits for a second round.
 int proj32_splits(const Geo& g) {
-    const int cus = device_cus();
+    const int cus = device_cu_count();
     int s;
     if (big_tiles(g)) {
         const int tiles = 2 * ((g.r + WM - 1) / WM) * (g.HD / WN);

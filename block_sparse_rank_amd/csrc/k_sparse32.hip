@@ -925,15 +925,8 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
 
 // Attention work-groups on the current device: one per CU, at most kSparseMaxWg.
 int sparse_wgs() {
-    static int cache[64] = {0};
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return kSparseMaxWg;
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-        cus = kSparseMaxWg;
-    const int G = cus < kSparseMaxWg ? cus : kSparseMaxWg;
-    if (dev >= 0 && dev < 64) cache[dev] = G;
-    return G;
+    const int cus = device_cu_count();
+    return cus < kSparseMaxWg ? cus : kSparseMaxWg;
 }
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }

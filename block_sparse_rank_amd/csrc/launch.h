@@ -4,6 +4,10 @@
 
 #include "common.h"
 
+// Compute units of the current device, looked up once per device (a
+// lock-free cache: concurrent first calls store the same value atomically).
+int device_cu_count();
+
 // Epilogue of the attention kernels.
 //  o_main : f32 [Lq][H][d] receives O (NULL: not written)
 //  out    : dtype [Lq][H][d] receives the gated fusion g*O + (1-g)*o_lin (NULL: no fusion)

@@ -49,7 +49,7 @@ ENTRY_FORWARD = 6
 EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
-    "hsa_linear_branch", "hsa_fuse", "hsa_forward",
+    "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
 ]
 
 
@@ -91,6 +91,12 @@ class Outputs(ctypes.Structure):
         "o_linear", "gate")]
 
 
+class Fork(ctypes.Structure):
+    """hsakv_fork: a caller-owned second stream and two events (hipStream_t,
+    hipEvent_t handles) for hsa_forward's low-rank branch."""
+    _fields_ = [("stream", c_void_p), ("fork", c_void_p), ("join", c_void_p)]
+
+
 _P = c_void_p
 _D = ctypes.POINTER(Dims)
 _sig = {
@@ -106,7 +112,9 @@ _sig = {
     "hsa_linear_branch": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_fuse": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs), _P,
-                              c_size_t, _P]),
+                              c_size_t, _P, ctypes.POINTER(Fork)]),
+    "hsakv_fork_create": (c_int32, [ctypes.POINTER(Fork)]),
+    "hsakv_fork_destroy": (c_int32, [ctypes.POINTER(Fork)]),
 }
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
@@ -227,11 +235,23 @@ def hsa_fuse(dims: Dims, q, w_g, b_g, o_sparse, o_linear, out, gate=None, stream
         _ptr(out), _ptr(gate), _stream(stream)))
 
 
+def fork_create() -> Fork:
+    """A new fork (second stream and two events) on the current device."""
+    f = Fork()
+    _check("hsakv_fork_create", _lib.hsakv_fork_create(ctypes.byref(f)))
+    return f
+
+
+def fork_destroy(f: Fork) -> None:
+    _check("hsakv_fork_destroy", _lib.hsakv_fork_destroy(ctypes.byref(f)))
+
+
 def hsa_forward(dims: Dims, tau, cur_prompt: int, inputs: dict, outputs: dict, ws,
-                stream=None) -> None:
+                stream=None, fork: Optional[Fork] = None) -> None:
     ins = Inputs(*[_ptr(inputs.get(n)) for n, _ in Inputs._fields_])
     outs = Outputs(*[_ptr(outputs.get(n)) for n, _ in Outputs._fields_])
     w, wb = _ws(ws)
     _check("hsa_forward", _lib.hsa_forward(
         ctypes.byref(dims), ctypes.cast(_host_f32(tau), c_void_p), int(cur_prompt),
-        ctypes.byref(ins), ctypes.byref(outs), w, wb, _stream(stream)))
+        ctypes.byref(ins), ctypes.byref(outs), w, wb, _stream(stream),
+        ctypes.byref(fork) if fork is not None else None))

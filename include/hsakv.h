@@ -54,7 +54,9 @@
  *    HSAKV_ERR_HIP and hsakv_last_hip_error() gives the hipError_t of the
  *    calling thread.
  *  - Thread safety: reentrant; calls on different streams may overlap if
- *    their output and workspace buffers are disjoint.
+ *    their output and workspace buffers are disjoint. The only state kept
+ *    between calls is the compute-unit count of each device, looked up once
+ *    and cached atomically.
  */
 #ifndef HSAKV_H
 #define HSAKV_H
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HSAKV_VERSION 1
+#define HSAKV_VERSION 2
 
 /* status codes */
 #define HSAKV_OK                   0
@@ -92,7 +94,10 @@ extern "C" {
 
 /* Sizes of one chunk-layer; all host integers. Supported: d in {64, 128};
  * Bq = 64; Binter and Bintra multiples of 64 up to 512; r a multiple of 32
- * up to 1024; NB_max <= 4096; 1 <= Kp <= 64; 1 <= P <= 65536; H <= 1024. */
+ * up to 1024; NB_max <= 4096; 1 <= Kp <= 64; 1 <= P <= 65536; H <= 256 and
+ * H * d <= 16384; r * L * (bytes per element) < 2^31 (E and F are addressed
+ * with 32-bit byte offsets). Anything else returns HSAKV_ERR_UNSUPPORTED or
+ * HSAKV_ERR_BAD_DIMS. */
 typedef struct hsakv_dims {
     int32_t H;                /* attention heads */
     int32_t d;                /* head dimension */
@@ -138,6 +143,20 @@ typedef struct hsakv_outputs {
     float*   gate;       /* [Lq][H] f32 */
 } hsakv_outputs;
 
+/* A second stream and two events for hsa_forward, owned by the caller.
+ * `stream` is a hipStream_t on the device of the call's stream; `fork` and
+ * `join` are hipEvent_t (timing disabled is enough). hsa_forward records
+ * `fork` on its stream after the gather, makes `stream` wait on it, runs the
+ * low-rank branch there, records `join` on `stream` and makes its own stream
+ * wait on `join` before the attention: all of the call's work stays ordered
+ * on the call's stream. One fork serves one call at a time: calls that
+ * overlap in time (several host threads) each need their own. */
+typedef struct hsakv_fork {
+    void* stream;
+    void* fork;
+    void* join;
+} hsakv_fork;
+
 /* ---- helpers (host only; none touches the GPU) ---- */
 
 int         hsakv_version(void);
@@ -148,6 +167,17 @@ int         hsakv_last_hip_error(void);
 int         hsakv_validate(const hsakv_dims* dims);
 /* Workspace bytes `entry` needs for these dims (0 if dims are invalid). */
 size_t      hsakv_workspace_bytes(const hsakv_dims* dims, int32_t entry);
+
+/* Creates the stream (non-blocking, default priority) and the two events of
+ * a fork on the current device; the caller owns them and releases them with
+ * hsakv_fork_destroy. These two calls are the only ones that create HIP
+ * objects; they are set-up calls, made once, never on the hot path.
+ * Returns HSAKV_OK, HSAKV_ERR_NULL_ARG or HSAKV_ERR_HIP (nothing is left
+ * created on an error). */
+int hsakv_fork_create(hsakv_fork* fork);
+/* Destroys what hsakv_fork_create made (after the work that uses it is
+ * done) and clears the struct. */
+int hsakv_fork_destroy(hsakv_fork* fork);
 
 /* ---- entry points ---- */
 
@@ -235,15 +265,14 @@ int hsa_fuse(const hsakv_dims* dims, const void* q, const float* w_g, const floa
  * attention's epilogue. Results equal the separate entry points run in that
  * order. tau (host, H floats) and cur_prompt (host) as above. Workspace:
  * HSAKV_ENTRY_FORWARD.
- * For bf16 the low-rank branch runs on a second, library-owned stream of
- * the current device (one per device, default priority), forked from
- * `stream` after the gather and joined back into it with events before the
- * attention, so all of the call's work is still ordered on `stream`. Calls
- * from several host threads on one device share that stream: they stay
- * correct but serialise their low-rank branches. */
+ * `fork` (host, nullable): with a fork whose stream is set and bf16 data, the
+ * low-rank branch runs on the fork's stream beside the selection (see
+ * hsakv_fork); NULL, or a fork with a NULL stream, runs everything on
+ * `stream`. The results are the same either way. float32 data always runs on
+ * `stream`. */
 int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
                 const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
-                void* stream);
+                void* stream, const hsakv_fork* fork);
 
 #ifdef __cplusplus
 }

@@ -114,12 +114,14 @@ def page_scores(page_kmean: np.ndarray, qbar: np.ndarray, pages: Sequence[int]) 
     """O4. Page-level score s_p = sum over heads and dims of kbar[p] * qbar (reading R2).
 
     Returned rounded to float32: the ranking decision is taken in the
-    kernels' precision.
+    kernels' precision. A score that is not a number (a page mean or a query
+    holding an infinity or a NaN) is taken as -infinity, so such a page
+    ranks below every page with a number (reading R24).
     """
     out = {}
     for p in pages:
         s = float(np.sum(page_kmean[p] * qbar))
-        out[p] = float(np.float32(s))
+        out[p] = -math.inf if math.isnan(s) else float(np.float32(s))
     return out
 
 

@@ -111,6 +111,14 @@ def check_selection(cnt: np.ndarray, idx: np.ndarray, mass: np.ndarray, sel, tau
     return differ
 
 
+def masked_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, ids, blocks) -> np.ndarray:
+    """Library check, independent of the oracle: float64 attention of q [n][d]
+    over the tokens of blocks `ids` of K, V [L][d] (torch's SDPA)."""
+    J = np.concatenate([np.arange(blocks[b][0], blocks[b][1]) for b in ids])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(K[J]), t(V[J]))[0, 0].numpy()
+
+
 def pack_selection(sel, NB_max: int):
     """Oracle selection lists -> (sel_count [H][NQB], sel_idx [H][NQB][NB_max]) int32."""
     H, NQB = len(sel), len(sel[0])
@@ -124,17 +132,31 @@ def pack_selection(sel, NB_max: int):
     return cnt, idx
 
 
+_FORK = None
+
+
+def default_fork() -> "hs.Fork":
+    """One fork (second stream and two events) for this process's tests, as a
+    caller that keeps one for its forwards would."""
+    global _FORK
+    if _FORK is None:
+        _FORK = hs.fork_create()
+    return _FORK
+
+
 class Case:
     """Inputs of one chunk-layer on the host (storage arrays) and on the device."""
 
     def __init__(self, s: synth.Shape, chunk: dict | None = None, pool=None, cur_prompt=None,
-                 page_prompt=None):
+                 page_prompt=None, tau=None):
         self.s = s
         self.d = dims_of(s)
         assert hs.validate(self.d) == hs.OK
         self.ch = chunk if chunk is not None else synth.draw_chunk(s)
         if page_prompt is not None:
             self.ch["page_prompt"] = np.asarray(page_prompt, np.int32)
+        if tau is not None:
+            self.ch["tau"] = np.asarray(tau, np.float32)
         self.cur_prompt = s.cur_prompt if cur_prompt is None else cur_prompt
         self.pool_k, self.pool_v = pool if pool is not None else synth.draw_pool(s)
         ch = self.ch
@@ -204,7 +226,7 @@ class Case:
         hs.hsa_fuse(d, self.t["q"], self.t["w_g"], self.t["b_g"], o_s, o_l, out, gate)
         return out, gate
 
-    def forward(self, page_kmean, debug=True):
+    def forward(self, page_kmean, debug=True, fork="default"):
         s, d = self.s, self.d
         outs = {"out": torch.zeros((s.Lq, s.H, s.d), dtype=tdtype(s), device="cuda")}
         if debug:
@@ -222,5 +244,8 @@ class Case:
         ins = {k: self.t[k] for k in ("q", "k_intra", "v_intra", "pool_k", "pool_v", "E", "F",
                                       "w_g", "b_g", "page_prompt")}
         ins["page_kmean"] = page_kmean
-        hs.hsa_forward(d, self.ch["tau"], self.cur_prompt, ins, outs, ws(d, hs.ENTRY_FORWARD))
+        if fork == "default":
+            fork = default_fork()
+        hs.hsa_forward(d, self.ch["tau"], self.cur_prompt, ins, outs, ws(d, hs.ENTRY_FORWARD),
+                       fork=fork)
         return outs

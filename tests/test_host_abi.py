@@ -38,7 +38,7 @@ def test_header_declares_exactly_the_exports():
 
 
 def test_version_and_status_strings():
-    assert hs.version() == 1
+    assert hs.version() == 2
     for code in range(-8, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
@@ -75,11 +75,22 @@ def test_workloads_validate(name):
     (dict(H=300, d=64), hs.ERR_UNSUPPORTED),
     (dict(tokens_per_frame=1 << 28), hs.ERR_BAD_DIMS),
     (dict(Kp=44), hs.ERR_UNSUPPORTED),            # NB_max above 4096
+    # E and F past 2^31 bytes (32-bit byte offsets in the projection):
+    # r = 1024, L = 8 * 131072 + 64 columns of bf16
+    (dict(r=1024, Kp=8, tokens_per_frame=16384, Binter=512, Lq=64), hs.ERR_UNSUPPORTED),
 ])
 def test_validation_errors(over, code):
     d = _dims(**over)
     assert hs.validate(d) == code
     assert hs.workspace_bytes(d, hs.ENTRY_FORWARD) == 0
+
+
+def test_projection_byte_limit_boundary():
+    """r * L * 2 bytes just below 2^31 validates; the first r above does not."""
+    d = _dims(r=992, Kp=8, tokens_per_frame=16384, Binter=512, Lq=64)
+    assert 992 * d.L * 2 < 2 ** 31 and hs.validate(d) == hs.OK
+    d = _dims(r=1024, Kp=8, tokens_per_frame=16384, Binter=512, Lq=64)
+    assert 1024 * d.L * 2 >= 2 ** 31 and hs.validate(d) == hs.ERR_UNSUPPORTED
 
 
 def test_null_dims():
@@ -124,6 +135,19 @@ def test_entry_points_reject_before_launch():
     # forward: null struct members
     _expect(hs.ERR_NULL_ARG, hs.hsa_forward, d, [0.5] * H, 0, {"q": FAKE}, {"out": FAKE}, None,
             stream=0)
+    # forward: a fork with a stream but no events
+    full = {n: FAKE for n, _ in hs.Inputs._fields_}
+    half_fork = hs.Fork(FAKE, None, None)
+    _expect(hs.ERR_NULL_ARG, hs.hsa_forward, d, [0.5] * H, 0, full, {"out": FAKE}, None,
+            stream=0, fork=half_fork)
+    # forward: every argument valid but the workspace one byte short, or
+    # misaligned: rejected on the host, nothing is enqueued
+    need = hs.workspace_bytes(d, hs.ENTRY_FORWARD)
+    for ws_ptr, nbytes in ((FAKE, need - 1), (FAKE + 16, need), (None, need)):
+        st = hs._lib.hsa_forward(ctypes.byref(d), ctypes.cast(hs._host_f32([0.5] * H), ctypes.c_void_p),
+                                 0, ctypes.byref(hs.Inputs(*[FAKE] * len(hs.Inputs._fields_))),
+                                 ctypes.byref(hs.Outputs(FAKE)), ws_ptr, nbytes, None, None)
+        assert st == hs.ERR_WORKSPACE
     # no launch happened, so no HIP error was recorded
     assert hs._lib.hsakv_last_hip_error() == 0
 

@@ -96,6 +96,20 @@ MUTATIONS = [
     ("fusion with the branches swapped",
      "return gg * o_s + (1.0 - gg) * o_l", "return gg * o_l + (1.0 - gg) * o_s",
      [pins.test_gate_matches_expit_and_isolates_branches]),
+    ("forward projects K with F and V with E",
+     "E_act = as_f64(E, dtype)[:, cols]\n    F_act = as_f64(F, dtype)[:, cols]",
+     "E_act = as_f64(F, dtype)[:, cols]\n    F_act = as_f64(E, dtype)[:, cols]",
+     [pins.test_forward_one_hot_projection_with_an_absent_slot]),
+    ("key sequence puts the chunk before the history",
+     "return np.concatenate([hist, intra], axis=0)", "return np.concatenate([intra, hist], axis=0)",
+     [pins.test_forward_identity_projection_is_history_then_chunk,
+      lambda: pins.test_forward_sparse_branch_is_masked_attention_over_history_then_chunk(0.35, 6, None)]),
+    ("forward keeps the absent slots' columns",
+     "cols = active_projection_columns(n_sel, Kp, Tp, Lq)", "cols = np.arange(n_sel * Tp + Lq)",
+     [pins.test_forward_one_hot_projection_with_an_absent_slot]),
+    ("forward pools the chunk keys as history blocks",
+     "blocks = block_table(Lh, Lq, Binter, Bintra)", "blocks = block_table(Lh, Lq, Binter, Binter)",
+     [lambda: pins.test_forward_sparse_branch_is_masked_attention_over_history_then_chunk(0.35, 6, None)]),
     ("page summary sums instead of averaging",
      "return pool_k.mean(axis=1)", "return pool_k.sum(axis=1)",
      [pins.test_page_summary_closed_forms]),

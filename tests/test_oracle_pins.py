@@ -100,6 +100,27 @@ def test_retrieval_duplicate_tie_goes_low():
     assert idx.tolist() == [1] and n == 1
 
 
+def test_retrieval_nan_scores_rank_last():
+    """Pages whose score is not a number rank below every finite score; among
+    themselves the lower page goes first (worked by hand: finite scores of
+    pages 0, 2, 4 are 1, 3, 2)."""
+    kmean = np.zeros((5, 1, 2))
+    kmean[0] = [[1.0, 0.0]]
+    kmean[1] = [[np.nan, 0.0]]
+    kmean[2] = [[3.0, 0.0]]
+    kmean[3] = [[np.inf, -np.inf]]        # inf - inf: NaN
+    kmean[4] = [[2.0, 0.0]]
+    q = np.array([[1.0, 1.0]])
+    prompts = np.zeros(5, np.int32)
+    assert oracle.retrieve(kmean, prompts, 0, q, 2)[0].tolist() == [2, 4]
+    assert oracle.retrieve(kmean, prompts, 0, q, 3)[0].tolist() == [0, 2, 4]
+    assert oracle.retrieve(kmean, prompts, 0, q, 4)[0].tolist() == [0, 1, 2, 4]
+    idx, n = oracle.retrieve(kmean, prompts, 0, q, 5)
+    assert idx.tolist() == [0, 1, 2, 3, 4] and n == 5
+    # only NaN candidates: the lowest indices
+    assert oracle.retrieve(kmean, np.array([1, 0, 1, 0, 1], np.int32), 0, q, 1)[0].tolist() == [1]
+
+
 def test_gather_is_a_bit_copy():
     s = synth.shape("tiny")
     pk, _ = synth.draw_pool(s)
@@ -354,6 +375,124 @@ def test_tiny_forward_gate_limits():
     assert np.array_equal(hi["out"], hi["o_sparse"])
     _, _, _, _, lo = _tiny_forward(b_g=np.full(s.H, -1e3, np.float32))
     assert np.array_equal(lo["out"], lo["o_linear"])
+
+
+# ---------------------------------------------------------------------------
+# whole forward: how the branches are wired (key order, E against K and F
+# against V, the columns of absent slots). Every expected value below is
+# built by the test itself from the pool pages and the chunk, never from the
+# oracle's own intermediates.
+
+def _forward_f32(s, ch, pk, pv, **kw):
+    return oracle.forward(
+        dtype=s.dtype, q=ch["q"], k_intra=ch["k_intra"], v_intra=ch["v_intra"], pool_k=pk,
+        pool_v=pv, page_prompt=ch["page_prompt"], cur_prompt=s.cur_prompt, E=ch["E"], F=ch["F"],
+        w_g=ch["w_g"], b_g=ch["b_g"], tau=ch["tau"], Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra,
+        Bq=s.Bq, **kw)
+
+
+def _keys_by_hand(pk, pv, ch, page_idx):
+    """[history pages in slot order ; chunk] along tokens, float64, built here."""
+    K = np.concatenate([pk[int(p)] for p in page_idx] + [ch["k_intra"]]).astype(np.float64)
+    V = np.concatenate([pv[int(p)] for p in page_idx] + [ch["v_intra"]]).astype(np.float64)
+    return K, V
+
+
+def test_forward_identity_projection_is_history_then_chunk():
+    """r = L and E = F = I with every slot present: the projected keys and
+    values are the key sequence itself, history slots first, then the chunk,
+    and the low-rank branch is dense attention over it."""
+    s = synth.shape("tiny").with_(seed=41)
+    ch = synth.draw_chunk(s)
+    pk, pv = synth.draw_pool(s)
+    L = s.L
+    ch["E"] = np.eye(L, dtype=np.float32)
+    ch["F"] = np.eye(L, dtype=np.float32)
+    r = _forward_f32(s, ch, pk, pv)
+    assert r["n_sel"] == s.Kp
+    K, V = _keys_by_hand(pk, pv, ch, r["page_idx"])
+    assert np.array_equal(r["k_low"], K) and np.array_equal(r["v_low"], V)
+    q = ch["q"].astype(np.float64)
+    for h in range(s.H):
+        assert np.allclose(r["o_linear"][:, h], _sdpa(q[:, h], K[:, h], V[:, h]),
+                           rtol=1e-12, atol=1e-13)
+
+
+def test_forward_one_hot_projection_with_an_absent_slot():
+    """One matching page for Kp = 2 slots: slot 1 is absent and its E/F
+    columns face no key. One-hot rows of E and of F (different columns for
+    the two) pick a history token of the present slot, a chunk token, and a
+    column of the absent slot (a zero row of K' or V')."""
+    s = synth.shape("tiny").with_(P=3, seed=42)
+    ch = synth.draw_chunk(s)
+    ch["page_prompt"] = np.array([1, 0, 1], np.int32)      # only page 1 matches prompt 0
+    pk, pv = synth.draw_pool(s)
+    Tp, Lq, L = s.Tp, s.Lq, s.L
+    assert L == 2 * Tp + Lq
+    ek = [5, 2 * Tp + 44, Tp + 2, 127, 2 * Tp + 255]       # slot 0 t5, chunk t44, absent, slot 0 t127, chunk t255
+    fv = [17, 2 * Tp + 4, Tp + 100, 2 * Tp, 0]
+    E = np.zeros((len(ek), L), np.float32)
+    F = np.zeros((len(fv), L), np.float32)
+    E[np.arange(len(ek)), ek] = 1.0
+    F[np.arange(len(fv)), fv] = 1.0
+    ch["E"], ch["F"] = E, F
+    r = _forward_f32(s.with_(r=len(ek)), ch, pk, pv)
+    assert r["n_sel"] == 1 and r["page_idx"].tolist() == [1]
+
+    def pick(col, page, chunk):
+        if col < Tp:
+            return page[col].astype(np.float64)
+        if col >= 2 * Tp:
+            return chunk[col - 2 * Tp].astype(np.float64)
+        return np.zeros(page.shape[1:])                     # absent slot
+
+    Kw = np.stack([pick(c, pk[1], ch["k_intra"]) for c in ek])
+    Vw = np.stack([pick(c, pv[1], ch["v_intra"]) for c in fv])
+    assert np.array_equal(r["k_low"], Kw) and np.array_equal(r["v_low"], Vw)
+    q = ch["q"].astype(np.float64)
+    for h in range(s.H):
+        assert np.allclose(r["o_linear"][:, h], _sdpa(q[:, h], Kw[:, h], Vw[:, h]),
+                           rtol=1e-12, atol=1e-13)
+
+
+def _blocks_by_hand(Lh, Lq, Binter, Bintra):
+    hist = [(a, min(a + Binter, Lh)) for a in range(0, Lh, Binter)]
+    chunk = [(Lh + a, Lh + min(a + Bintra, Lq)) for a in range(0, Lq, Bintra)]
+    return hist + chunk
+
+
+@pytest.mark.parametrize("tau0,P,prompts", [(0.35, 6, None), (0.6, 3, [1, 0, 1])])
+def test_forward_sparse_branch_is_masked_attention_over_history_then_chunk(tau0, P, prompts):
+    """A tau < 1 head: the forward's block masses are the softmax of pooled
+    logits over test-built blocks of [history ; chunk], and its sparse output
+    is dense attention masked to the tokens of the forward's selected blocks
+    of that same sequence."""
+    s = synth.shape("tiny").with_(P=P, seed=43)
+    ch = synth.draw_chunk(s)
+    if prompts is not None:
+        ch["page_prompt"] = np.array(prompts, np.int32)
+    ch["tau"] = np.array([tau0, 1.0], np.float32)
+    pk, pv = synth.draw_pool(s)
+    r = _forward_f32(s, ch, pk, pv)
+    K, V = _keys_by_hand(pk, pv, ch, r["page_idx"])
+    Lh = r["n_sel"] * s.Tp
+    blocks = _blocks_by_hand(Lh, s.Lq, s.Binter, s.Bintra)
+    q = ch["q"].astype(np.float64)
+    for h in range(s.H):
+        kb = np.stack([K[a:b, h].mean(axis=0) for a, b in blocks])
+        for i in range(-(-s.Lq // s.Bq)):
+            q0, q1 = i * s.Bq, min((i + 1) * s.Bq, s.Lq)
+            qb = q[q0:q1, h].mean(axis=0)
+            want_mass = scipy.special.softmax(kb @ qb / math.sqrt(s.d))
+            assert np.allclose(r["mass"][h, i], want_mass, rtol=1e-12, atol=1e-15)
+            ids = r["sel"][h][i]
+            if tau0 < 1.0 and h == 0:
+                assert len(ids) < len(blocks)               # a real subset
+            mask = np.zeros((q1 - q0, K.shape[0]), dtype=bool)
+            for b in ids:
+                mask[:, blocks[b][0]:blocks[b][1]] = True
+            want = _sdpa(q[q0:q1, h], K[:, h], V[:, h], mask)
+            assert np.allclose(r["o_sparse"][q0:q1, h], want, rtol=1e-12, atol=1e-13)
 
 
 def test_bf16_decode_is_exact():
