@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -225,6 +226,7 @@ HSAKV_API const char* hsakv_status_str(int s) {
         case HSAKV_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
         case HSAKV_ERR_HIP: return "HIP launch failed";
         case HSAKV_ERR_UNSUPPORTED: return "unsupported dimensions";
+        case HSAKV_ERR_TOO_LARGE: return "scratch needed exceeds the static scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }
@@ -530,5 +532,71 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         launch_sparse_attn<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel,
                                   sel_count, sel_idx, sparse_ws, ep, st);
     }
+    return done();
+}
+
+// ---- allocation-free variant of hsa_sparse_attn ----------------------------------
+//
+// Its scratch (the work plan and the split-group softmax partials) lives in a
+// fixed device array of HSAKV_STATIC_SCRATCH_BYTES, one copy per GPU for the
+// life of the process. Host code never passes the array's name to a kernel:
+// the name is a host-side stand-in; the device address of each GPU's copy is
+// looked up once per device and kept.
+
+static __device__ __align__(256) unsigned char scratch[HSAKV_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of this device's `scratch`, looked up on the first call on
+// the device (with that device current). nullptr with the HIP error recorded
+// if the lookup fails.
+void* static_scratch() {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_hip_error = (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+HSAKV_API int hsa_sparse_attn_static(const hsakv_dims* dims, const void* q, const void* k_hist,
+                                     const void* v_hist, const void* k_intra, const void* v_intra,
+                                     const int32_t* n_sel, const int32_t* sel_count,
+                                     const int32_t* sel_idx, float* o_sparse, void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(q && k_hist && v_hist && k_intra && v_intra && n_sel && sel_count && sel_idx &&
+                      o_sparse,
+                  HSAKV_ERR_NULL_ARG);
+    HSAKV_REQUIRE(aligned(q) && aligned(k_hist) && aligned(v_hist) && aligned(k_intra) &&
+                      aligned(v_intra) && aligned(o_sparse) && aligned(n_sel, 4) &&
+                      aligned(sel_count, 4) && aligned(sel_idx, 4),
+                  HSAKV_ERR_MISALIGNED);
+    const Geo g = make_geo(dims);
+    if (ws_sparse(g) > (size_t)HSAKV_STATIC_SCRATCH_BYTES) return HSAKV_ERR_TOO_LARGE;
+    void* ws = static_scratch();
+    if (!ws) return HSAKV_ERR_HIP;
+    Epi ep{o_sparse, nullptr, nullptr, nullptr, nullptr, nullptr};
+    hipStream_t st = (hipStream_t)stream;
+    if (dims->dtype == HSAKV_BF16)
+        launch_sparse_attn<bf16_t>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
+                                   sel_idx, ws, ep, st);
+    else
+        launch_sparse_attn<float>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
+                                  sel_idx, ws, ep, st);
     return done();
 }

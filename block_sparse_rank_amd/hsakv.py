@@ -38,6 +38,8 @@ ERR_WORKSPACE = -5
 ERR_MISALIGNED = -6
 ERR_HIP = -7
 ERR_UNSUPPORTED = -8
+ERR_TOO_LARGE = -9
+STATIC_SCRATCH_BYTES = 128 << 20
 F32 = 0
 BF16 = 1
 ENTRY_GATHER = 1
@@ -50,6 +52,7 @@ EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
     "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
+    "hsa_sparse_attn_static",
 ]
 
 
@@ -113,6 +116,7 @@ _sig = {
     "hsa_fuse": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs), _P,
                               c_size_t, _P, ctypes.POINTER(Fork)]),
+    "hsa_sparse_attn_static": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hsakv_fork_create": (c_int32, [ctypes.POINTER(Fork)]),
     "hsakv_fork_destroy": (c_int32, [ctypes.POINTER(Fork)]),
 }
@@ -218,6 +222,15 @@ def hsa_sparse_attn(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_
     _check("hsa_sparse_attn", _lib.hsa_sparse_attn(
         ctypes.byref(dims), _ptr(q), _ptr(k_hist), _ptr(v_hist), _ptr(k_intra), _ptr(v_intra),
         _ptr(n_sel), _ptr(sel_count), _ptr(sel_idx), _ptr(o_sparse), w, wb, _stream(stream)))
+
+
+def hsa_sparse_attn_static(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
+                           sel_idx, o_sparse, stream=None) -> None:
+    """hsa_sparse_attn with its scratch in the library's fixed device array:
+    no workspace, no allocation."""
+    _check("hsa_sparse_attn_static", _lib.hsa_sparse_attn_static(
+        ctypes.byref(dims), _ptr(q), _ptr(k_hist), _ptr(v_hist), _ptr(k_intra), _ptr(v_intra),
+        _ptr(n_sel), _ptr(sel_count), _ptr(sel_idx), _ptr(o_sparse), _stream(stream)))
 
 
 def hsa_linear_branch(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, E, F, o_linear,

@@ -80,6 +80,10 @@ extern "C" {
 #define HSAKV_ERR_MISALIGNED      -6
 #define HSAKV_ERR_HIP             -7
 #define HSAKV_ERR_UNSUPPORTED     -8
+#define HSAKV_ERR_TOO_LARGE       -9   /* scratch beyond HSAKV_STATIC_SCRATCH_BYTES */
+
+/* Size of the fixed device scratch of hsa_sparse_attn_static (per GPU). */
+#define HSAKV_STATIC_SCRATCH_BYTES (128u << 20)
 
 /* element types */
 #define HSAKV_F32   0
@@ -240,6 +244,24 @@ int hsa_sparse_attn(const hsakv_dims* dims, const void* q, const void* k_hist, c
                     const void* k_intra, const void* v_intra, const int32_t* n_sel,
                     const int32_t* sel_count, const int32_t* sel_idx, float* o_sparse,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* hsa_sparse_attn without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,
+ * layouts and results are those of hsa_sparse_attn (the same kernels).
+ * Scratch: a fixed array of HSAKV_STATIC_SCRATCH_BYTES in device memory,
+ * one per GPU, held until the process ends; dims whose plan and partials
+ * need more (hsakv_workspace_bytes(dims, HSAKV_ENTRY_SPARSE) larger than
+ * that) return HSAKV_ERR_TOO_LARGE before anything is enqueued. The first
+ * call on a device looks up that device's copy of the array (no
+ * allocation). Every call on a GPU shares its array and leaves its contents
+ * behind; nothing in it must start at zero. Calls that overlap in time on
+ * one GPU (several streams or host threads) race on the array and must be
+ * serialised by the caller. */
+int hsa_sparse_attn_static(const hsakv_dims* dims, const void* q, const void* k_hist,
+                           const void* v_hist, const void* k_intra, const void* v_intra,
+                           const int32_t* n_sel, const int32_t* sel_count, const int32_t* sel_idx,
+                           float* o_sparse, void* stream);
 
 /* Linformer-style low-rank global branch (HSA paragraph; the Linformer paper
  * on the citation map). One E and one F, shared by every head:

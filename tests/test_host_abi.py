@@ -39,7 +39,7 @@ def test_header_declares_exactly_the_exports():
 
 def test_version_and_status_strings():
     assert hs.version() == 2
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
     assert hs._lib.hsakv_last_hip_error() == 0
@@ -91,6 +91,23 @@ def test_projection_byte_limit_boundary():
     assert 992 * d.L * 2 < 2 ** 31 and hs.validate(d) == hs.OK
     d = _dims(r=1024, Kp=8, tokens_per_frame=16384, Binter=512, Lq=64)
     assert 1024 * d.L * 2 >= 2 ** 31 and hs.validate(d) == hs.ERR_UNSUPPORTED
+
+
+def test_static_sparse_rejects_what_exceeds_its_scratch():
+    """The allocation-free attention refuses dims whose plan and partials
+    need more than its fixed scratch, on the host, before any launch."""
+    big = _dims(H=96, Lq=10800, tokens_per_frame=3600, Kp=6, r=512)
+    assert hs.validate(big) == hs.OK
+    assert hs.workspace_bytes(big, hs.ENTRY_SPARSE) > hs.STATIC_SCRATCH_BYTES
+    _expect(hs.ERR_TOO_LARGE, hs.hsa_sparse_attn_static, big, *([FAKE] * 9), stream=0)
+    for name in ("wan1.3b-480p", "wan14b-720p-90s"):
+        import synth
+        s = synth.shape(name)
+        d = hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize,
+                         P=s.P, Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r,
+                         dtype=s.dtype)
+        assert hs.workspace_bytes(d, hs.ENTRY_SPARSE) <= hs.STATIC_SCRATCH_BYTES
+    assert hs._lib.hsakv_last_hip_error() == 0
 
 
 def test_null_dims():
