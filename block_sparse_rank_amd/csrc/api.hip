@@ -108,7 +108,7 @@ int done() {
 
 // ---- workspace sizes -------------------------------------------------------
 
-size_t ws_gather(const Geo& g) { return align_up(((size_t)retrieve_slabs(g) + 1) * g.HD * 4); }
+size_t ws_gather(const Geo& g) { return align_up((size_t)retrieve_slabs(g) * g.HD * 4); }
 
 size_t ws_select(const Geo& g) {
     return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4) +

@@ -8,40 +8,23 @@
 #include "launch.h"
 
 // ---------------------------------------------------------------------------
-// Retrieval, step 1: partial column sums of q over token slabs (k_item_colsum,
-// below).
+// Retrieval, step 1: partial column sums of q over token slabs (k_q_colsum,
+// below). The chunk mean is their sum in slab order, taken by step 2.
 
-int retrieve_slabs(const Geo& g) {
-    int slabs = (g.Lq + 63) / 64;
-    return slabs > 64 ? 64 : slabs;
-}
-
-
-// ---------------------------------------------------------------------------
-// Retrieval, step 2: chunk-mean query, one column per thread, slab partials
-// added in slab order.
-
-__global__ void __launch_bounds__(256)
-k_qbar(const float* __restrict__ partial, int slabs, int HD, float inv_Lq, float* __restrict__ qbar) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= HD) return;
-    float v[64];
-#pragma unroll
-    for (int k = 0; k < 64; ++k) v[k] = k < slabs ? partial[(size_t)k * HD + c] : 0.f;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < 64; ++k) s += v[k];
-    qbar[c] = s * inv_Lq;
-}
+// Always 32 slabs (slabs past the chunk hold zero sums), so the chunk-mean
+// kernel loads every partial unconditionally.
+constexpr int kSlabs = 32;
+int retrieve_slabs(const Geo&) { return kSlabs; }
 
 // ---------------------------------------------------------------------------
-// Retrieval, step 3 (one block of 1024 threads): page scores, prompt filter,
-// top-Kp with ties to the lower page, slots ascending.
+// Retrieval, step 2 (one block of 1024 threads): the chunk-mean query (slab
+// partials added in slab order, one column per thread), page scores, prompt
+// filter, top-Kp with ties to the lower page, slots ascending.
 
 constexpr int kRetrieveThreads = 1024;
 
 __global__ void __launch_bounds__(kRetrieveThreads)
-k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
+k_retrieve(const float* __restrict__ partial, int slabs, float inv_Lq, int HD, int P, int Kp,
            const float* __restrict__ page_kmean, const int32_t* __restrict__ page_prompt,
            int cur_prompt, int32_t* __restrict__ page_idx, int32_t* __restrict__ n_sel) {
     extern __shared__ float smem[];
@@ -55,43 +38,74 @@ k_retrieve(const float* __restrict__ qbar_g, int HD, int P, int Kp,
     const int wave = tid >> 6;
     const int nwaves = kRetrieveThreads / 64;
 
-    for (int c = tid; c < HD; c += kRetrieveThreads) qbar[c] = qbar_g[c];
+    // columns tid and tid + 1024: both columns' slab partials in flight at once
+    (void)slabs;
+    for (int c = tid; c < HD; c += 2 * kRetrieveThreads) {
+        const int c2 = c + kRetrieveThreads < HD ? c + kRetrieveThreads : c;
+        float v[kSlabs], w[kSlabs];
+#pragma unroll
+        for (int k = 0; k < kSlabs; ++k) {
+            v[k] = partial[(size_t)k * HD + c];
+            w[k] = partial[(size_t)k * HD + c2];
+        }
+        float sv = 0.f, sw = 0.f;
+#pragma unroll
+        for (int k = 0; k < kSlabs; ++k) {
+            sv += v[k];
+            sw += w[k];
+        }
+        qbar[c] = sv * inv_Lq;
+        if (c + kRetrieveThreads < HD) qbar[c2] = sw * inv_Lq;
+    }
     if (tid == 0) n_cand = 0;
     __syncthreads();
 
     // page scores, one wave per page; lanes take columns lane, lane + 64, ...
-    // in a fixed order (up to 24 independent loads in flight), then a fixed tree
-    for (int p = wave; p < P; p += nwaves) {
-        const bool match = page_prompt[p] == cur_prompt;
-        float s = 0.f;
-        if (match) {
-            const float* km = page_kmean + (size_t)p * HD;
-            int c = lane;
-            for (; c + 23 * 64 < HD; c += 24 * 64) {   // 24 loads in flight (one pass at H d = 1536)
-                float k24[24];
+    // in a fixed order, then a fixed tree. A wave holds two pages at a time
+    // (pages w and w + 16), with both pages' loads in flight together.
+    for (int p0 = wave; p0 < P; p0 += 2 * nwaves) {
+        const int p1 = p0 + nwaves;
+        const bool m0 = page_prompt[p0] == cur_prompt;
+        const bool m1 = p1 < P && page_prompt[p1] == cur_prompt;
+        float s0 = 0.f, s1 = 0.f;
+        int c = lane;
+        const float* k0 = page_kmean + (size_t)p0 * HD;
+        const float* k1 = page_kmean + (size_t)(p1 < P ? p1 : p0) * HD;
+        // every page is loaded (a page past P reloads p0); only matching
+        // pages' scores are kept
+        for (; c + 23 * 64 < HD; c += 24 * 64) {
+            float a[24], b[24];
 #pragma unroll
-                for (int u = 0; u < 24; ++u) k24[u] = km[c + 64 * u];
-#pragma unroll
-                for (int u = 0; u < 24; ++u) s = fmaf(k24[u], qbar[c + 64 * u], s);
+            for (int u = 0; u < 24; ++u) {
+                a[u] = k0[c + 64 * u];
+                b[u] = k1[c + 64 * u];
             }
-            for (; c + 7 * 64 < HD; c += 8 * 64) {
-                float k8[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) k8[u] = km[c + 64 * u];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) s = fmaf(k8[u], qbar[c + 64 * u], s);
+            for (int u = 0; u < 24; ++u) {
+                s0 = fmaf(a[u], qbar[c + 64 * u], s0);
+                s1 = fmaf(b[u], qbar[c + 64 * u], s1);
             }
-            for (; c < HD; c += 64) s = fmaf(km[c], qbar[c], s);
-            s = wave_sum(s);
-            // a score that is not a number ranks below every number: with
-            // -inf the rank test below is a total order (ties to the lower
-            // page), so exactly min(Kp, candidates) pages are chosen
-            if (__builtin_isnan(s)) s = -INFINITY;
         }
+        for (; c < HD; c += 64) {
+            s0 = fmaf(k0[c], qbar[c], s0);
+            s1 = fmaf(k1[c], qbar[c], s1);
+        }
+        s0 = wave_sum(s0);
+        s1 = wave_sum(s1);
+        // a score that is not a number ranks below every number: with -inf
+        // the rank test below is a total order (ties to the lower page), so
+        // exactly min(Kp, candidates) pages are chosen
+        if (__builtin_isnan(s0)) s0 = -INFINITY;
+        if (__builtin_isnan(s1)) s1 = -INFINITY;
         if (lane == 0) {
-            score[p] = s;
-            cand[p] = match ? 1 : 0;
-            if (match) atomicAdd(&n_cand, 1);
+            score[p0] = m0 ? s0 : 0.f;
+            cand[p0] = m0 ? 1 : 0;
+            if (m0) atomicAdd(&n_cand, 1);
+            if (p1 < P) {
+                score[p1] = m1 ? s1 : 0.f;
+                cand[p1] = m1 ? 1 : 0;
+                if (m1) atomicAdd(&n_cand, 1);
+            }
         }
     }
     __syncthreads();
@@ -132,13 +146,9 @@ size_t retrieve_smem_bytes(const Geo& g) {
 void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
                      const int32_t* page_prompt, int cur_prompt, int32_t* page_idx,
                      int32_t* n_sel, hipStream_t st) {
-    // the chunk mean goes right after the slab partials in the workspace
-    float* qbar = const_cast<float*>(partial) + (size_t)retrieve_slabs(g) * g.HD;
-    hipLaunchKernelGGL(k_qbar, dim3((g.HD + 255) / 256), dim3(256), 0, st, partial,
-                       retrieve_slabs(g), g.HD, 1.0f / (float)g.Lq, qbar);
-    hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st,
-                       (const float*)qbar, g.HD, g.P, g.Kp, page_kmean, page_prompt, cur_prompt,
-                       page_idx, n_sel);
+    hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st, partial,
+                       retrieve_slabs(g), 1.0f / (float)g.Lq, g.HD, g.P, g.Kp, page_kmean, page_prompt,
+                       cur_prompt, page_idx, n_sel);
 }
 
 // ---------------------------------------------------------------------------
@@ -379,13 +389,56 @@ void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hi
 template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
 template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
 
+// Slab column sums of q for the chunk mean: work-group (slab, 256 columns) of
+// 512 threads, 32 column lanes of 8 elements x 16 row groups, 16 rows (bf16;
+// 8 for f32) in flight per thread. Each thread keeps a Kahan sum per column
+// over its rows in row order; the 16 group sums are added in group order.
+constexpr int kQsumGroups = 16;
+
+template <typename T>
+__global__ void __launch_bounds__(32 * kQsumGroups)
+k_q_colsum(const T* __restrict__ q, int rows_per_slab, int Lq, int HD, float* __restrict__ partial) {
+    const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const int col0 = (blockIdx.y * 32 + lane) * 8;
+    const int r0 = blockIdx.x * rows_per_slab;
+    const int r1 = r0 + rows_per_slab < Lq ? r0 + rows_per_slab : Lq;
+    Kahan acc[8];
+    if (col0 < HD) {
+        constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
+        for (int t = r0 + grp; t < r1; t += kQsumGroups * kRows) {
+            Row8<T> v[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                if (t + kQsumGroups * u < r1) v[u].load(q + (long long)(t + kQsumGroups * u) * HD + col0);
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                if (t + kQsumGroups * u < r1) {
+                    float xv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    v[u].add_to(xv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e].add(xv[e]);
+                }
+        }
+    }
+    __shared__ float part[kQsumGroups][32 * 8 + 4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[grp][lane * 8 + e] = acc[e].s;
+    __syncthreads();
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (threadIdx.x < 256 && c < HD) {
+        Kahan k;
+#pragma unroll
+        for (int g2 = 0; g2 < kQsumGroups; ++g2) k.add(part[g2][threadIdx.x]);
+        partial[(size_t)blockIdx.x * HD + c] = k.s;
+    }
+}
+
 template <typename T>
 void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
     const int slabs = retrieve_slabs(g);
     const int per = (g.Lq + slabs - 1) / slabs;
     dim3 grid(slabs, (g.HD + 255) / 256);
-    hipLaunchKernelGGL(k_item_colsum<T>, grid, dim3(1024), 0, st, (const T*)q, (long long)per, (long long)g.Lq,
-                       g.HD, 1.0f, partial);
+    hipLaunchKernelGGL(k_q_colsum<T>, grid, dim3(32 * kQsumGroups), 0, st, (const T*)q, per, g.Lq, g.HD, partial);
 }
 template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
 template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);

@@ -366,12 +366,11 @@ HSAKV_DEV int block_excl_scan(int v, int* tot, int* wsum) {
 // some rows selected. Greedy, per head: a group starts from the lowest row
 // not yet grouped and takes, R - 1 times, the remaining row whose selection
 // shares the most tiles with the group's union less the tiles it would add.
-// grows[grp * R + r] = row (NQB past the head's rows). Heads with more than
-// 64 kGroupRowsPerLane rows or more than 32 kGroupWords tiles keep
-// consecutive rows. The grouping only orders the work: each row's result is
-// the same.
-constexpr int kGroupWords = 32;       // bitmask words per row (tiles per head <= 1024)
-constexpr int kGroupRowsPerLane = 2;  // rows per lane (rows per head <= 128)
+// grows[grp * R + r] = row (NQB past the head's rows). The row bitmasks take
+// W words (W = 32: at most 1024 tiles per head; 64: at most 2048) and a lane
+// holds RPL rows (2: at most 128 rows per head; 4: at most 256); heads past
+// the largest of these keep consecutive rows. The grouping only orders the
+// work: each row's result is the same.
 
 // Tiles of the head's key blocks, history blocks first: block b < NBh covers
 // tiles [th b, th (b + 1)), chunk block NBh + c covers th NBh + tc c onwards.
@@ -382,19 +381,21 @@ HSAKV_DEV int tiles_of_head(const Geo& g, int NBh, int& th, int& tc) {
 }
 
 // Selection of one row as a tile bitmask: work-group (h, i) writes
-// tbits[(h NQB + i) kGroupWords + w], bit t % 32 of word t / 32 set when the
-// row selected the block of tile t.
+// tbits[(h NQB + i) W + w], bit t % 32 of word t / 32 set when the row
+// selected the block of tile t.
+template <int W>
 __global__ void __launch_bounds__(64)
 k_plan_bits(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restrict__ sel_count,
             const int32_t* __restrict__ sel_idx, uint32_t* __restrict__ tbits) {
-    __shared__ uint32_t words[kGroupWords];
+    static_assert(W <= 64, "one word per lane");
+    __shared__ uint32_t words[W];
     const int row = blockIdx.x, lane = threadIdx.x;
     const int n_sel = *n_sel_p;
     const int NBh = hist_blocks(g, n_sel);
     const int NB = NBh + g.NBc;
     int th, tc;
-    if (tiles_of_head(g, NBh, th, tc) > 32 * kGroupWords) return;
-    if (lane < kGroupWords) words[lane] = 0u;
+    if (tiles_of_head(g, NBh, th, tc) > 32 * W) return;
+    if (lane < W) words[lane] = 0u;
     __syncthreads();
     const int c = sel_count[row];
     const int32_t* ids = sel_idx + (size_t)row * g.NB_max;
@@ -406,7 +407,7 @@ k_plan_bits(Geo g, const int32_t* __restrict__ n_sel_p, const int32_t* __restric
         for (int t = t0; t < t0 + nt; ++t) atomicOr(&words[t >> 5], 1u << (t & 31));
     }
     __syncthreads();
-    if (lane < kGroupWords) tbits[(size_t)row * kGroupWords + lane] = words[lane];
+    if (lane < W) tbits[(size_t)row * W + lane] = words[lane];
 }
 
 // Largest value over the wave, in every lane: DPP rotations within each row
@@ -425,15 +426,18 @@ HSAKV_DEV uint32_t wave_max_u32(uint32_t v) {
 }
 
 // One work-group per head, kGroupWaves waves: lane l of every wave holds rows
-// l and l + 64, wave v holds words [kWordsPerWave v, kWordsPerWave (v + 1))
-// of their bitmasks. The waves sum their partial overlaps through LDS; every
+// l, l + 64, ... (RPL of them), wave v holds words [W/4 v, W/4 (v + 1)) of
+// their bitmasks. The waves sum their partial overlaps through LDS; every
 // wave then takes the same pick.
 constexpr int kGroupWaves = 4;
-constexpr int kWordsPerWave = kGroupWords / kGroupWaves;
 
+template <int W, int RPL>
 __global__ void __launch_bounds__(64 * kGroupWaves)
 k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restrict__ tbits,
             int32_t* __restrict__ grows) {
+    constexpr int kWordsPerWave = W / kGroupWaves;
+    constexpr int kGroupRowsPerLane = RPL;
+    static_assert(RPL <= 4, "row ids of a head fit the 8-bit field of the pick key");
     __shared__ int part[2][kGroupWaves][64 * kGroupRowsPerLane];
     const int h = blockIdx.x, lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -443,23 +447,23 @@ k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restri
     int th, tc;
     const int NT = tiles_of_head(g, NBh, th, tc);
     int32_t* out = grows + (size_t)h * gph * R;
-    if (NT > 32 * kGroupWords || g.NQB > 64 * kGroupRowsPerLane) {
+    if (NT > 32 * W || g.NQB > 64 * kGroupRowsPerLane) {
         for (int e = threadIdx.x; e < gph * R; e += 64 * kGroupWaves) out[e] = e < g.NQB ? e : g.NQB;
         return;
     }
-    const int W = (NT + 31) >> 5;
+    const int Wn = (NT + 31) >> 5;   // words in use
     uint32_t bits[kGroupRowsPerLane][kWordsPerWave];
     bool left[kGroupRowsPerLane];
 #pragma unroll
     for (int k = 0; k < kGroupRowsPerLane; ++k) {
         const int row = lane + 64 * k;
         left[k] = row < g.NQB;
-        const uint32_t* src = tbits + (size_t)(h * g.NQB + (left[k] ? row : 0)) * kGroupWords;
+        const uint32_t* src = tbits + (size_t)(h * g.NQB + (left[k] ? row : 0)) * W;
         int cnt = 0;
 #pragma unroll
         for (int x = 0; x < kWordsPerWave; ++x) {
             const int w = kWordsPerWave * wv + x;
-            bits[k][x] = left[k] && w < W ? src[w] : 0u;
+            bits[k][x] = left[k] && w < Wn ? src[w] : 0u;
             cnt += __builtin_popcount(bits[k][x]);
         }
         part[1][wv][row] = cnt;
@@ -512,7 +516,9 @@ k_plan_rows(Geo g, const int32_t* __restrict__ n_sel_p, const uint32_t* __restri
             const int pl_ = pick & 63, pk = pick >> 6;
 #pragma unroll
             for (int x = 0; x < kWordsPerWave; ++x) {
-                const uint32_t v = pk ? bits[1][x] : bits[0][x];
+                uint32_t v = bits[0][x];
+#pragma unroll
+                for (int k = 1; k < kGroupRowsPerLane; ++k) v = pk == k ? bits[k][x] : v;   // fixed indices
                 const uint32_t bw = (uint32_t)__builtin_amdgcn_readlane((int)v, pl_);
                 uni[x] = r == 0 ? bw : (uni[x] | bw);
             }
@@ -941,6 +947,13 @@ struct SparseWs {
 };
 
 int n_groups(const Geo& g) { return g.H * ((g.NQB + R - 1) / R); }
+// Bitmask words per row of the row grouping: 32 up to 1024 tiles per head
+// (every history slot present), 64 up to 2048; past that the grouping keeps
+// consecutive rows and the bitmasks go unused.
+int plan_words(const Geo& g) {
+    const int tiles = ((g.Binter + KT - 1) / KT) * g.NBh_max + ((g.Bintra + KT - 1) / KT) * g.NBc;
+    return tiles <= 1024 ? 32 : 64;
+}
 // Tiles of a group's union at most (every block of the head selected).
 int tiles_per_group(const Geo& g) {
     return ((g.Binter + KT - 1) / KT) * g.NBh_max + ((g.Bintra + KT - 1) / KT) * g.NBc;
@@ -952,7 +965,7 @@ SparseWs carve(const Geo& g, void* ws) {
     const int NG = n_groups(g);
     char* p = (char*)ws;
     SparseWs s;
-    s.tbits = (uint32_t*)p;  p += al256((size_t)g.H * g.NQB * kGroupWords * 4);
+    s.tbits = (uint32_t*)p;  p += al256((size_t)g.H * g.NQB * plan_words(g) * 4);
     s.grows = (int32_t*)p;   p += al256((size_t)NG * R * 4);
     s.tdesc = (int2*)p;      p += al256((size_t)NG * tiles_per_group(g) * 8);
     s.gcount = (int32_t*)p;  p += al256((size_t)NG * 4);
@@ -967,7 +980,7 @@ SparseWs carve(const Geo& g, void* ws) {
 
 size_t sparse_bf16_ws_bytes(const Geo& g) {
     const int NG = n_groups(g);
-    return al256((size_t)g.H * g.NQB * kGroupWords * 4) + al256((size_t)NG * R * 4) +
+    return al256((size_t)g.H * g.NQB * plan_words(g) * 4) + al256((size_t)NG * R * 4) +
            al256((size_t)NG * tiles_per_group(g) * 8) + 2 * al256((size_t)NG * 4) +
            al256((size_t)(NG + 1) * 4) + part_o_bytes(g) + part_ml_bytes();
 }
@@ -978,9 +991,27 @@ void launch_sparse_plan_bf16(const Geo& g, const int32_t* n_sel, const int32_t* 
                              const int32_t* sel_idx, void* ws, hipStream_t st) {
     const int NG = n_groups(g);
     const SparseWs s = carve(g, ws);
-    hipLaunchKernelGGL(k_plan_bits, dim3(g.H * g.NQB), dim3(64), 0, st, g, n_sel, sel_count, sel_idx, s.tbits);
-    hipLaunchKernelGGL(k_plan_rows, dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel, (const uint32_t*)s.tbits,
-                       s.grows);
+    const int W = plan_words(g);
+    const bool wide_rows = g.NQB > 128;   // 4 rows per lane (up to 256 per head), else 2
+    if (W == 32) {
+        hipLaunchKernelGGL(k_plan_bits<32>, dim3(g.H * g.NQB), dim3(64), 0, st, g, n_sel, sel_count, sel_idx,
+                           s.tbits);
+        if (wide_rows)
+            hipLaunchKernelGGL((k_plan_rows<32, 4>), dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel,
+                               (const uint32_t*)s.tbits, s.grows);
+        else
+            hipLaunchKernelGGL((k_plan_rows<32, 2>), dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel,
+                               (const uint32_t*)s.tbits, s.grows);
+    } else {
+        hipLaunchKernelGGL(k_plan_bits<64>, dim3(g.H * g.NQB), dim3(64), 0, st, g, n_sel, sel_count, sel_idx,
+                           s.tbits);
+        if (wide_rows)
+            hipLaunchKernelGGL((k_plan_rows<64, 4>), dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel,
+                               (const uint32_t*)s.tbits, s.grows);
+        else
+            hipLaunchKernelGGL((k_plan_rows<64, 2>), dim3(g.H), dim3(64 * kGroupWaves), 0, st, g, n_sel,
+                               (const uint32_t*)s.tbits, s.grows);
+    }
     hipLaunchKernelGGL(k_plan_groups, dim3(NG), dim3(kPlanThreads), 0, st, g, n_sel, sel_count, sel_idx,
                        (const int32_t*)s.grows, s.tdesc, tiles_per_group(g), s.gcount, s.gtiles);
     hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, st, NG, (const int32_t*)s.gtiles, s.gstart);

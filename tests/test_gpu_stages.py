@@ -59,12 +59,17 @@ VARIANTS = [
                             tau_law="uniform", seed=29), {}),
     # the limits the 720p workload crosses, at a size the oracle finishes in
     # seconds: 129 query blocks (more than 128) and 1129 tiles per head (more
-    # than 1024) put the plan on four consecutive rows per group; 1129 blocks
-    # per row take the 32-items-per-lane selection; r = 512 on the 256 x 256
-    # projection (two row tiles)
+    # than 1024) take the plan's wide row grouping (64-word bitmasks, four
+    # rows per lane); 1129 blocks per row take the 32-items-per-lane
+    # selection; r = 512 on the 256 x 256 projection (two row tiles)
     ("bf16-limits", _variant("tiny", dtype="bf16", H=2, d=128, Lq=8256, tokens_per_frame=4000, Kp=2,
                              P=3, Binter=64, r=512, clustered=True, tau_law="uniform", seed=31),
      dict(tau=[0.35, 0.42])),
+    # 257 query blocks (more than 256): the plan keeps four consecutive rows
+    # per group
+    ("bf16-consecutive-rows", _variant("tiny", dtype="bf16", H=1, d=64, Lq=16448, tokens_per_frame=16, Kp=1,
+                                       P=2, r=64, clustered=True, tau_law="uniform", seed=33),
+     dict(tau=[0.35])),
 ]
 
 
