@@ -64,6 +64,7 @@ __all__ = [
     "gate",
     "fuse",
     "forward",
+    "page_commit",
 ]
 
 
@@ -408,3 +409,45 @@ def forward(*, dtype: str, q, k_intra, v_intra, pool_k, pool_v, page_prompt, cur
         "qb": qb, "kb": kb, "mass": mass, "sel": sel, "o_sparse": o_s, "o_linear": o_l,
         "k_low": k_low, "v_low": v_low, "gate": g, "out": out,
     }
+
+
+# ---------------------------------------------------------------------------
+# HKV page commit (news summary, HKV paragraph: history KV pairs partitioned
+# into semantic pages of Psize frames, each page indexed for the prompt-level
+# and page-level retrieval stages; project page, second figure caption)
+
+def page_commit(pool_k: np.ndarray, pool_v: np.ndarray, page_kmean: np.ndarray,
+                page_prompt: np.ndarray, k_chunk: np.ndarray, v_chunk: np.ndarray,
+                fill: int, cur_prompt: int):
+    """Append one chunk's keys and values to the page pool and finalise the
+    pages it completes.
+
+    The history is one token sequence cut into pages of Tp tokens, page p
+    holding tokens [p Tp, (p + 1) Tp); `fill` tokens are already committed,
+    so the chunk's token j becomes history token fill + j (reading R25). A
+    page is finalised by the commit that writes its last token: its
+    page-mean key (the metadata the page-level stage scores) is the mean of
+    its Tp keys, and it is tagged with that commit's prompt id (reading R26).
+    Pages not completed keep their mean and tag.
+
+    pool_k, pool_v: [P][Tp][H][d] storage arrays (bf16 bits or float32);
+    page_kmean [P][H][d] float64; page_prompt [P] int; k_chunk, v_chunk
+    [n][H][d] storage arrays. Returns new (pool_k, pool_v, page_kmean,
+    page_prompt, finalised page ids); the inputs are not modified.
+    """
+    P, Tp = pool_k.shape[0], pool_k.shape[1]
+    n = k_chunk.shape[0]
+    if fill < 0 or fill + n > P * Tp:
+        raise ValueError("the chunk does not fit in the pool")
+    pk, pv = pool_k.copy(), pool_v.copy()
+    km, pp = np.array(page_kmean, dtype=np.float64), np.array(page_prompt).copy()
+    for j in range(n):
+        t = fill + j
+        pk[t // Tp, t % Tp] = k_chunk[j]
+        pv[t // Tp, t % Tp] = v_chunk[j]
+    done = [p for p in range(P) if fill < (p + 1) * Tp <= fill + n]
+    dtype = "bf16" if pk.dtype == np.uint16 else "f32"
+    for p in done:
+        km[p] = page_summary(as_f64(pk[p], dtype)[None])[0]
+        pp[p] = cur_prompt
+    return pk, pv, km, pp, done

@@ -110,6 +110,14 @@ MUTATIONS = [
     ("forward pools the chunk keys as history blocks",
      "blocks = block_table(Lh, Lq, Binter, Bintra)", "blocks = block_table(Lh, Lq, Binter, Binter)",
      [lambda: pins.test_forward_sparse_branch_is_masked_attention_over_history_then_chunk(0.35, 6, None)]),
+    ("commit finalises a page one token early",
+     "done = [p for p in range(P) if fill < (p + 1) * Tp <= fill + n]",
+     "done = [p for p in range(P) if fill < (p + 1) * Tp <= fill + n + 1]",
+     [pins.test_commit_within_one_page_finalises_nothing,
+      pins.test_commit_across_a_page_end_finalises_it]),
+    ("commit writes the chunk one token late",
+     "        t = fill + j\n", "        t = fill + j + 1\n",
+     [pins.test_commit_within_one_page_finalises_nothing]),
     ("page summary sums instead of averaging",
      "return pool_k.mean(axis=1)", "return pool_k.sum(axis=1)",
      [pins.test_page_summary_closed_forms]),

@@ -504,3 +504,68 @@ def test_bf16_decode_is_exact():
     # round-to-nearest-even on a hand-made tie: 1 + 2^-8 sits halfway between
     # 1 and 1 + 2^-7, and goes to the even mantissa, 1
     assert oracle.as_f64(synth.round_bf16_bits(np.array([1 + 2 ** -8], np.float32)), "bf16")[0] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# page commit
+
+def _empty_pool(P, Tp, H, d):
+    return (np.zeros((P, Tp, H, d), np.float32), np.zeros((P, Tp, H, d), np.float32),
+            np.full((P, H, d), -7.0), np.full(P, -1, np.int32))
+
+
+def test_commit_within_one_page_finalises_nothing():
+    P, Tp, H, d = 3, 8, 2, 4
+    pk, pv, km, pp = _empty_pool(P, Tp, H, d)
+    k = np.arange(1, 5 * H * d + 1, dtype=np.float32).reshape(5, H, d)
+    v = -k
+    # tokens 2..6: the page's last token (7) is still missing
+    nk, nv, nkm, npp, done = oracle.page_commit(pk, pv, km, pp, k, v, fill=2, cur_prompt=5)
+    assert done == []
+    assert np.array_equal(nk[0, 2:7], k) and np.array_equal(nv[0, 2:7], v)
+    assert np.all(nk[0, :2] == 0) and np.all(nk[0, 7] == 0) and np.all(nk[1:] == 0)
+    assert np.array_equal(nkm, km) and np.array_equal(npp, pp)
+    assert np.all(pk == 0)                       # inputs untouched
+
+
+def test_commit_across_a_page_end_finalises_it():
+    """Tokens 6..10 of 8-token pages: page 0 fills (tokens 6, 7 close it),
+    page 1 receives tokens 8..10 and stays open."""
+    P, Tp, H, d = 3, 8, 1, 2
+    pk, pv, km, pp = _empty_pool(P, Tp, H, d)
+    first = np.full((6, H, d), 2.0, np.float32)
+    pk, pv, km, pp, done = oracle.page_commit(pk, pv, km, pp, first, first, fill=0, cur_prompt=1)
+    assert done == []
+    ramp = np.arange(5, dtype=np.float32)[:, None, None] * np.ones((5, H, d), np.float32)
+    pk, pv, km, pp, done = oracle.page_commit(pk, pv, km, pp, ramp, ramp, fill=6, cur_prompt=4)
+    assert done == [0]
+    # page 0 = six 2.0 tokens, then ramp values 0 and 1: mean (12 + 0 + 1) / 8
+    assert np.allclose(km[0], 13.0 / 8.0, rtol=0, atol=1e-15)
+    assert pp.tolist() == [4, -1, -1]
+    assert np.array_equal(km[1], np.full((H, d), -7.0))
+    assert np.array_equal(pk[1, :3, 0, 0], [2.0, 3.0, 4.0])
+
+
+def test_commit_of_chunks_equals_commit_of_their_concatenation():
+    """Three-frame chunks into eight-frame pages (the pages' 480p setting in
+    miniature): committing chunk by chunk equals committing all at once, and
+    after 8 chunks exactly 3 pages are finalised."""
+    rng = np.random.default_rng(9)
+    P, Tp, H, d, n = 4, 16, 2, 4, 6          # a frame of 2 tokens; page = 8 frames, chunk = 3
+    pk, pv, km, pp = _empty_pool(P, Tp, H, d)
+    chunks = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(8)]
+    fill, all_done = 0, []
+    for c in chunks:
+        pk, pv, km, pp, done = oracle.page_commit(pk, pv, km, pp, c, -c, fill, cur_prompt=3)
+        fill += n
+        all_done += done
+    assert all_done == [0, 1, 2]
+    qk, qv, qkm, qpp, qdone = oracle.page_commit(*_empty_pool(P, Tp, H, d), np.concatenate(chunks),
+                                                 -np.concatenate(chunks), 0, cur_prompt=3)
+    assert qdone == [0, 1, 2]
+    assert np.array_equal(qk, pk) and np.array_equal(qv, pv)
+    assert np.array_equal(qkm[:3], km[:3]) and qpp.tolist() == pp.tolist() == [3, 3, 3, -1]
+    # a finalised page's mean is the page summary of the page
+    assert np.allclose(km[1], oracle.page_summary(pk[1:2].astype(np.float64))[0], rtol=0, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.page_commit(pk, pv, km, pp, chunks[0], chunks[0], P * Tp - 2, 0)
