@@ -65,6 +65,8 @@ __all__ = [
     "fuse",
     "forward",
     "page_commit",
+    "POLICIES",
+    "splitmix64_at",
 ]
 
 
@@ -126,18 +128,59 @@ def page_scores(page_kmean: np.ndarray, qbar: np.ndarray, pages: Sequence[int]) 
     return out
 
 
-def retrieve(page_kmean: np.ndarray, page_prompt: np.ndarray, cur_prompt: int,
-             qbar: np.ndarray, Kp: int) -> Tuple[np.ndarray, int]:
-    """O3-O5. Two-stage retrieval of the top-Kp pages.
+# Retrieval policies: the method's two-stage retrieval and the alternatives
+# the pages compare it with under the same page budget (news summary, HKV
+# paragraph, Table 6: page-only, prompt-only, recent-page, random-page and
+# mismatched-page retrieval; Table 5: a sliding window of recent frames,
+# which is the recent-page policy).
+POLICIES = ("two_stage", "page_only", "prompt_only", "recent", "random", "mismatched")
 
-    Candidates are the prompt-matching pages; they are ordered by score,
-    higher first, equal scores to the lower page index; the first
-    min(Kp, |candidates|) are kept and put in ascending page order, which
-    is their slot order in the active cache (reading R3).
+
+def splitmix64_at(seed: int, i: int) -> int:
+    """Output i (0-based) of the SplitMix64 generator seeded with `seed`
+    (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+    OOPSLA 2014): state seed + (i + 1) * 0x9E3779B97F4A7C15 mod 2^64, then
+    the generator's output mix."""
+    M = (1 << 64) - 1
+    z = (seed + (i + 1) * 0x9E3779B97F4A7C15) & M
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M
+    return z ^ (z >> 31)
+
+
+def retrieve(page_kmean: np.ndarray, page_prompt: np.ndarray, cur_prompt: int,
+             qbar: np.ndarray, Kp: int, policy: str = "two_stage",
+             seed: int = 0) -> Tuple[np.ndarray, int]:
+    """O3-O5. Retrieval of Kp pages.
+
+    two_stage (the method): candidates are the prompt-matching pages; they
+    are ordered by score, higher first, equal scores to the lower page
+    index; the first min(Kp, |candidates|) are kept and put in ascending
+    page order, which is their slot order in the active cache (reading R3).
+    The alternatives change only the candidates and the ranking key
+    (reading R27): page_only ranks every page by score; prompt_only keeps the
+    Kp most recent (highest-index) matching pages; recent the Kp most recent
+    pages; random every page by the top 24 bits of SplitMix64 output p for
+    the given seed (so a draw is reproducible); mismatched ranks the pages of
+    other prompts by score.
     Returns (page_idx int32 [n_sel], n_sel).
     """
-    cand = prompt_filter(page_prompt, cur_prompt)
-    s = page_scores(page_kmean, qbar, cand)
+    P = len(page_prompt)
+    if policy in ("two_stage", "prompt_only"):
+        cand = prompt_filter(page_prompt, cur_prompt)
+    elif policy == "mismatched":
+        match = set(prompt_filter(page_prompt, cur_prompt))
+        cand = [p for p in range(P) if p not in match]
+    elif policy in ("page_only", "recent", "random"):
+        cand = list(range(P))
+    else:
+        raise ValueError(policy)
+    if policy in ("two_stage", "page_only", "mismatched"):
+        s = page_scores(page_kmean, qbar, cand)
+    elif policy in ("prompt_only", "recent"):
+        s = {p: float(p) for p in cand}
+    else:
+        s = {p: float(splitmix64_at(seed, p) >> 40) for p in cand}
     ranked = sorted(cand, key=lambda p: (-s[p], p))
     chosen = sorted(ranked[:Kp])
     return np.array(chosen, dtype=np.int32), len(chosen)
@@ -345,7 +388,8 @@ def fuse(g: np.ndarray, o_s: np.ndarray, o_l: np.ndarray) -> np.ndarray:
 
 def forward(*, dtype: str, q, k_intra, v_intra, pool_k, pool_v, page_prompt, cur_prompt: int,
             E, F, w_g, b_g, tau, Kp: int, Binter: int, Bintra: int, Bq: int,
-            page_kmean=None, heads=None, rows=None) -> Dict[str, object]:
+            page_kmean=None, heads=None, rows=None, policy: str = "two_stage",
+            seed: int = 0) -> Dict[str, object]:
     """O1-O13 for one chunk-layer, returning every intermediate.
 
     Tensors arrive in their storage type (bf16 as uint16 bits, f32 as
@@ -354,7 +398,8 @@ def forward(*, dtype: str, q, k_intra, v_intra, pool_k, pool_v, page_prompt, cur
     `heads` restricts the per-head stages to a subset (retrieval always uses
     every head); `rows` further restricts the sparse branch to a list of
     (h, i) rows. The pool may be a [P][Tp][H][d] array or a callable
-    returning page p's [Tp][H][d] storage array.
+    returning page p's [Tp][H][d] storage array. `policy` and `seed` select
+    the retrieval policy (two-stage by default).
     """
     qf = as_f64(q, dtype)
     Lq, H, d = qf.shape
@@ -367,7 +412,7 @@ def forward(*, dtype: str, q, k_intra, v_intra, pool_k, pool_v, page_prompt, cur
         page_kmean = np.stack([page_summary(as_f64(page(pool_k, p), dtype)[None])[0]
                                for p in range(P)])
     qbar = chunk_query_mean(qf)
-    page_idx, n_sel = retrieve(page_kmean, page_prompt, cur_prompt, qbar, Kp)
+    page_idx, n_sel = retrieve(page_kmean, page_prompt, cur_prompt, qbar, Kp, policy, seed)
 
     hsel = list(range(H)) if heads is None else list(heads)
     Tp = page(pool_k, 0).shape[0]

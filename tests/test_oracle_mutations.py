@@ -118,6 +118,15 @@ MUTATIONS = [
     ("commit writes the chunk one token late",
      "        t = fill + j\n", "        t = fill + j + 1\n",
      [pins.test_commit_within_one_page_finalises_nothing]),
+    ("prompt-only keeps the oldest matching pages",
+     "        s = {p: float(p) for p in cand}", "        s = {p: -float(p) for p in cand}",
+     [lambda: pins.test_retrieval_policies_hand_worked("prompt_only", 2, [2, 3])]),
+    ("mismatched keeps the matching pages",
+     "        cand = [p for p in range(P) if p not in match]", "        cand = sorted(match)",
+     [lambda: pins.test_retrieval_policies_hand_worked("mismatched", 2, [4, 5])]),
+    ("SplitMix64 with a wrong shift",
+     "z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M", "z = ((z ^ (z >> 28)) * 0x94D049BB133111EB) & M",
+     [pins.test_splitmix64_published_outputs]),
     ("page summary sums instead of averaging",
      "return pool_k.mean(axis=1)", "return pool_k.sum(axis=1)",
      [pins.test_page_summary_closed_forms]),

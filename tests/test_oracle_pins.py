@@ -569,3 +569,53 @@ def test_commit_of_chunks_equals_commit_of_their_concatenation():
     assert np.allclose(km[1], oracle.page_summary(pk[1:2].astype(np.float64))[0], rtol=0, atol=1e-15)
     with pytest.raises(ValueError):
         oracle.page_commit(pk, pv, km, pp, chunks[0], chunks[0], P * Tp - 2, 0)
+
+
+# ---------------------------------------------------------------------------
+# retrieval policies
+
+def test_splitmix64_published_outputs():
+    """The first outputs of SplitMix64 seeded with 0, as published with the
+    generator's reference implementation."""
+    assert oracle.splitmix64_at(0, 0) == 0xE220A8397B1DCDAF
+    assert oracle.splitmix64_at(0, 1) == 0x6E789E6AA1B965F4
+    assert oracle.splitmix64_at(0, 2) == 0x06C45D188009454F
+    # output i of seed s is output i + 1 of seed s - golden ratio increment
+    g = 0x9E3779B97F4A7C15
+    assert oracle.splitmix64_at((5 - g) % 2 ** 64, 4) == oracle.splitmix64_at(5, 3)
+
+
+def _policy_pool():
+    # scores with qbar = e0 (one head): pages 0..5 score 1, -1, 0, 2, 1, 3
+    kmean = np.zeros((6, 1, 2))
+    kmean[:, 0, 0] = [1.0, -1.0, 0.0, 2.0, 1.0, 3.0]
+    prompts = np.array([0, 1, 0, 0, 1, 1], np.int32)   # current prompt 0: pages 0, 2, 3
+    return kmean, prompts, np.array([[1.0, 0.0]])
+
+
+@pytest.mark.parametrize("policy,Kp,want", [
+    ("two_stage", 2, [0, 3]),          # matching 0, 2, 3 by score 1, 0, 2: 3 then 0
+    ("page_only", 2, [3, 5]),          # all pages: 5 (3), 3 (2)
+    ("page_only", 3, [0, 3, 5]),       # then the tie 0/4 at 1 goes to 0
+    ("prompt_only", 2, [2, 3]),        # two most recent matching
+    ("recent", 2, [4, 5]),
+    ("recent", 9, [0, 1, 2, 3, 4, 5]),
+    ("mismatched", 2, [4, 5]),         # pages 1, 4, 5 of other prompts: 5 (3), 4 (1)
+    ("mismatched", 4, [1, 4, 5]),
+])
+def test_retrieval_policies_hand_worked(policy, Kp, want):
+    kmean, prompts, q = _policy_pool()
+    idx, n = oracle.retrieve(kmean, prompts, 0, q, Kp, policy)
+    assert idx.tolist() == want and n == len(want)
+
+
+def test_random_policy_follows_its_keys():
+    kmean, prompts, q = _policy_pool()
+    for seed in (0, 1, 12345):
+        keys = [oracle.splitmix64_at(seed, p) >> 40 for p in range(6)]
+        want = sorted(sorted(range(6), key=lambda p: (-keys[p], p))[:3])
+        assert oracle.retrieve(kmean, prompts, 0, q, 3, "random", seed)[0].tolist() == want
+    a = oracle.retrieve(kmean, prompts, 0, q, 3, "random", 7)[0].tolist()
+    assert a == oracle.retrieve(kmean, prompts, 0, q, 3, "random", 7)[0].tolist()
+    with pytest.raises(ValueError):
+        oracle.retrieve(kmean, prompts, 0, q, 3, "nearest")
