@@ -45,6 +45,14 @@ def parse():
     ap.add_argument("--no-stages", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle sparse-attention rows in the CPU baseline sample")
+    ap.add_argument("--policy", default="two_stage",
+                    choices=["two_stage", "page_only", "prompt_only", "recent", "random", "mismatched"],
+                    help="retrieval policy of the forward (the method's is two_stage)")
+    ap.add_argument("--seed", type=int, default=0, help="seed of the random retrieval policy")
+    ap.add_argument("--sweep", default=None, choices=["psize-kp", "policies"],
+                    help="instead of the benchmark line, one JSON line per configuration: "
+                         "(Psize, Kp) at a fixed history length, or every retrieval policy on the "
+                         "60 s workload")
     return ap.parse_args()
 
 
@@ -60,96 +68,20 @@ def main() -> int:
     import synth
     from block_sparse_rank_amd import hsakv as hs
 
+    if a.sweep:
+        return sweep(a)
     over = {} if a.tau_min is None else {"tau_min": a.tau_min}
     s = synth.shape(a.workload, **over)
-    d = hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize,
-                     P=s.P, Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r,
-                     dtype=s.dtype)
-    assert hs.validate(d) == hs.OK
-    t0 = time.time()
-    ch = synth.draw_chunk(s)
-    pool_k, pool_v = synth.draw_pool(s)
-    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
-    dev = torch.device("cuda:0")
-
-    def up(x):
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(x).to(dev)
-
-    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
-    T = {k: up(ch[k]) for k in ("q", "k_intra", "v_intra", "E", "F", "w_g", "b_g", "page_prompt")}
-    T["pool_k"], T["pool_v"] = up(pool_k), up(pool_v)
-    page_kmean = torch.empty((s.P, s.H, s.d), dtype=torch.float32, device=dev)
-    hs.hkv_page_summary(d, T["pool_k"], page_kmean)          # commit-time metadata, untimed
-
-    out = torch.empty((s.Lq, s.H, s.d), dtype=tdt, device=dev)
-    sel_count = torch.empty((s.H, d.NQB), dtype=torch.int32, device=dev)
-    sel_idx = torch.empty((s.H, d.NQB, d.NB_max), dtype=torch.int32, device=dev)
-    n_sel = torch.empty((1,), dtype=torch.int32, device=dev)
-    ws_fwd = torch.empty(hs.workspace_bytes(d, hs.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
-    ins = {k: T[k] for k in ("q", "k_intra", "v_intra", "pool_k", "pool_v", "E", "F", "w_g",
-                             "b_g", "page_prompt")}
-    ins["page_kmean"] = page_kmean
-    outs = {"out": out, "sel_count": sel_count, "sel_idx": sel_idx, "n_sel": n_sel}
-    tau = ch["tau"]
-    stream = torch.cuda.current_stream()
-    fork = hs.fork_create()          # the caller-owned second stream of the forward
-
-    def step():
-        hs.hsa_forward(d, tau, s.cur_prompt, ins, outs, ws_fwd, stream=stream, fork=fork)
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # headline: each step timed alone by HIP events on the launch stream, with
-    # 1 GiB written before it (outside the events) so that no input or
-    # intermediate is left in the 256 MB MALL or the L2 caches
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(a.steps):
-        flush.fill_(k & 0xff)
-        evs[k][0].record(stream)
-        step()
-        evs[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t_start) * 1e3 / a.steps
-    cold = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    ms_med, ms_p10, ms_p90 = (float(np.percentile(cold, q)) for q in (50, 10, 90))
-
-    # secondary: the same steps back to back (warm caches), mean per step
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(stream)
-    for _ in range(a.steps):
-        step()
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    warm_ms = ev[0].elapsed_time(ev[1]) / a.steps
-    del flush
+    run = time_forward(s, a.steps, a.warmup, a.policy, a.seed)
+    d, T, ch, pool_k, pool_v = run["d"], run["T"], run["ch"], run["pool_k"], run["pool_v"]
+    page_kmean, tau, stream = run["page_kmean"], run["tau"], run["stream"]
+    n_sel, sel_count, sel_idx = run["n_sel"], run["sel_count"], run["sel_idx"]
+    ms_med, ms_p10, ms_p90, warm_ms, wall_ms = (run[k] for k in ("ms_med", "ms_p10", "ms_p90", "warm_ms",
+                                                                  "wall_ms"))
 
     # selection actually taken: algorithmic work of the sparse attention
-    n = int(n_sel.cpu()[0])
-    cnt = sel_count.cpu().numpy()
-    ids = sel_idx.cpu().numpy()
-    Lh = n * s.Tp
-    NBh = -(-Lh // s.Binter)
-    blen = np.array([min(s.Binter, Lh - b * s.Binter) for b in range(NBh)] +
-                    [min(s.Bintra, s.Lq - j * s.Bintra) for j in range(d.NBc)], dtype=np.int64)
-    qlen = np.array([min(s.Bq, s.Lq - i * s.Bq) for i in range(d.NQB)], dtype=np.int64)
-    pairs = 0
-    nsel_blocks = 0
-    for h in range(s.H):
-        for i in range(d.NQB):
-            c = int(cnt[h, i])
-            nsel_blocks += c
-            pairs += int(qlen[i]) * int(blen[ids[h, i, :c]].sum())
-    density = nsel_blocks / (s.H * d.NQB * (NBh + d.NBc))
-    sparse_flops = 4.0 * s.d * pairs                        # QK^T and PV, 2 flops per MAC
+    # (4 d flops per selected (query, key) pair: QK^T and PV, 2 flops per MAC)
+    density, sparse_flops, n = density_of(s, d, n_sel, sel_count, sel_idx)
     eb = 2 if s.dtype == "bf16" else 4
     gather_bytes = 2.0 * 2 * n * s.Tp * s.H * s.d * eb       # K and V, read + write
     floor_us, floor_parts = forward_floor(s, n, sparse_flops)
@@ -186,13 +118,186 @@ def main() -> int:
     if not a.no_stages:
         result.update(stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops,
                                   gather_bytes))
+        result["page_commit"] = commit_time(a, s, T, hs, torch, stream)
 
+    if a.policy != "two_stage":
+        result["config"]["retrieval_policy"] = a.policy
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, ch, pool_k, pool_v, a.cpu_budget)
         result["cpu_baseline"]["ratio_to_gpu"] = round(result["cpu_baseline"]["value"] / ms_med, 1)
-    hs.fork_destroy(fork)
+    hs.fork_destroy(run["fork"])
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_forward(s, steps, warmup, policy="two_stage", seed=0):
+    """Upload the synthetic chunk-layer `s`, then time hsa_forward on it: each
+    step alone by HIP events on the launch stream, 1 GiB written before it
+    (outside the events) so that no input or intermediate is left in the
+    256 MB MALL or the L2 caches; then the same steps back to back (warm)."""
+    import torch
+
+    import synth
+    from block_sparse_rank_amd import hsakv as hs
+
+    d = hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize,
+                     P=s.P, Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r,
+                     dtype=s.dtype)
+    assert hs.validate(d) == hs.OK
+    t0 = time.time()
+    ch = synth.draw_chunk(s)
+    pool_k, pool_v = synth.draw_pool(s)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    T = {k: up(ch[k]) for k in ("q", "k_intra", "v_intra", "E", "F", "w_g", "b_g", "page_prompt")}
+    T["pool_k"], T["pool_v"] = up(pool_k), up(pool_v)
+    page_kmean = torch.empty((s.P, s.H, s.d), dtype=torch.float32, device=dev)
+    hs.hkv_page_summary(d, T["pool_k"], page_kmean)          # commit-time metadata, untimed
+
+    out = torch.empty((s.Lq, s.H, s.d), dtype=tdt, device=dev)
+    sel_count = torch.empty((s.H, d.NQB), dtype=torch.int32, device=dev)
+    sel_idx = torch.empty((s.H, d.NQB, d.NB_max), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((1,), dtype=torch.int32, device=dev)
+    ws_fwd = torch.empty(hs.workspace_bytes(d, hs.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
+    ins = {k: T[k] for k in ("q", "k_intra", "v_intra", "pool_k", "pool_v", "E", "F", "w_g",
+                             "b_g", "page_prompt")}
+    ins["page_kmean"] = page_kmean
+    outs = {"out": out, "sel_count": sel_count, "sel_idx": sel_idx, "n_sel": n_sel}
+    tau = ch["tau"]
+    stream = torch.cuda.current_stream()
+    fork = hs.fork_create()          # the caller-owned second stream of the forward
+
+    def step():
+        hs.hsa_forward(d, tau, s.cur_prompt, ins, outs, ws_fwd, stream=stream, fork=fork,
+                       policy=policy, seed=seed)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        flush.fill_(k & 0xff)
+        evs[k][0].record(stream)
+        step()
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / steps
+    cold = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ms_med, ms_p10, ms_p90 = (float(np.percentile(cold, q)) for q in (50, 10, 90))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    warm_ms = ev[0].elapsed_time(ev[1]) / steps
+    del flush
+    return {"d": d, "T": T, "ch": ch, "pool_k": pool_k, "pool_v": pool_v, "page_kmean": page_kmean,
+            "tau": tau, "stream": stream, "fork": fork, "n_sel": n_sel, "sel_count": sel_count,
+            "sel_idx": sel_idx, "ms_med": ms_med, "ms_p10": ms_p10, "ms_p90": ms_p90,
+            "warm_ms": warm_ms, "wall_ms": wall_ms}
+
+
+def density_of(s, d, n_sel, sel_count, sel_idx):
+    """Selected-block density and algorithmic sparse flops of the selection taken."""
+    n = int(n_sel.cpu()[0])
+    cnt = sel_count.cpu().numpy()
+    ids = sel_idx.cpu().numpy()
+    Lh = n * s.Tp
+    NBh = -(-Lh // s.Binter)
+    blen = np.array([min(s.Binter, Lh - b * s.Binter) for b in range(NBh)] +
+                    [min(s.Bintra, s.Lq - j * s.Bintra) for j in range(d.NBc)], dtype=np.int64)
+    qlen = np.array([min(s.Bq, s.Lq - i * s.Bq) for i in range(d.NQB)], dtype=np.int64)
+    pairs, nb = 0, 0
+    for h in range(s.H):
+        for i in range(d.NQB):
+            c = int(cnt[h, i])
+            nb += c
+            pairs += int(qlen[i]) * int(blen[ids[h, i, :c]].sum())
+    return nb / (s.H * d.NQB * (NBh + d.NBc)), 4.0 * s.d * pairs, n
+
+
+def sweep(a):
+    """One JSON line per configuration (not the benchmark contract line).
+
+    psize-kp: the Wan-1.3B 480p chunk-layer with Psize in {4, 8, 16} frames
+    and Kp in {2, 4, 8}, the pool holding the same 256 frames of history
+    (P = 256 / Psize pages); the open (Psize, Kp) question of the pages,
+    timing and density only.
+    policies: the 60 s workload (6 prompt segments of 16 pages, the current
+    prompt's pages non-recent) under each retrieval policy.
+    """
+    from block_sparse_rank_amd import hsakv as hs
+
+    import synth
+    if a.sweep == "psize-kp":
+        base = synth.shape("wan1.3b-480p")
+        confs = [(dict(Psize=ps, P=256 // ps, Kp=kp), "two_stage") for ps in (4, 8, 16) for kp in (2, 4, 8)
+                 if ps * kp <= 64]
+    else:
+        base = synth.shape("wan1.3b-480p-60s")
+        confs = [({}, pol) for pol in ("two_stage", "page_only", "prompt_only", "recent", "random",
+                                       "mismatched")]
+    for over, pol in confs:
+        s = base.with_(**over)
+        run = time_forward(s, a.steps, a.warmup, pol, a.seed)
+        dens, flops, n = density_of(s, run["d"], run["n_sel"], run["sel_count"], run["sel_idx"])
+        line = {"sweep": a.sweep, "workload": s.name, "Psize": s.Psize, "Kp": s.Kp, "P": s.P,
+                "Tp": s.Tp, "policy": pol, "n_sel": n, "selected_block_density": round(dens, 4),
+                "median_ms": round(run["ms_med"], 4), "p10_ms": round(run["ms_p10"], 4),
+                "p90_ms": round(run["ms_p90"], 4), "warm_mean_ms": round(run["warm_ms"], 4),
+                "sparse_tflops": round(flops / (run["ms_med"] * 1e-3) / 1e12, 1)}
+        hs.fork_destroy(run["fork"])
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+def commit_time(a, s, T, hs, torch, stream):
+    """hkv_page_commit of this chunk's K and V into a two-page pool, placed so
+    that it completes page 0 (the copy plus one page-mean pass); HIP events
+    on the launch stream, mean over the repetitions."""
+    dev = T["q"].device
+    d2 = hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize, P=2,
+                      Kp=min(s.Kp, 2), Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r, dtype=s.dtype)
+    pk = torch.zeros((2, s.Tp, s.H, s.d), dtype=T["q"].dtype, device=dev)
+    pv = torch.zeros_like(pk)
+    km = torch.zeros((2, s.H, s.d), dtype=torch.float32, device=dev)
+    pp = torch.zeros(2, dtype=torch.int32, device=dev)
+    fill = max(0, s.Tp - s.Lq // 4)
+    n = min(s.Lq, 2 * s.Tp - fill)
+    ws = torch.empty(hs.workspace_bytes(d2, hs.ENTRY_COMMIT), dtype=torch.uint8, device=dev)
+
+    def once():
+        hs.hkv_page_commit(d2, pk, pv, km, pp, T["k_intra"], T["v_intra"], n, fill, 0, ws=ws, stream=stream)
+
+    once()
+    torch.cuda.synchronize()
+    reps = max(3, a.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        once()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    eb = 2 if s.dtype == "bf16" else 4
+    completes = (fill + n) // s.Tp - fill // s.Tp
+    nbytes = 2.0 * 2 * n * s.H * s.d * eb + completes * s.Tp * s.H * s.d * eb
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "tokens": n, "pages_completed": completes, "bound": "hbm",
+            "algorithmic_bytes": nbytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def forward_floor(s, n_sel, sparse_flops):

@@ -150,12 +150,33 @@ struct Carver {
 
 // ---- typed bodies ------------------------------------------------------------
 
+// Retrieval policy and seed (two-stage when the caller passes none).
+struct Policy {
+    int policy = HSAKV_POLICY_TWO_STAGE;
+    unsigned long long seed = 0;
+};
+
+Policy policy_of(const hsakv_retrieval* r) {
+    Policy p;
+    if (r) {
+        p.policy = r->policy;
+        p.seed = r->seed;
+    }
+    return p;
+}
+
+int check_policy(const hsakv_retrieval* r) {
+    if (r && (r->policy < HSAKV_POLICY_TWO_STAGE || r->policy > HSAKV_POLICY_MISMATCHED))
+        return HSAKV_ERR_UNSUPPORTED;
+    return HSAKV_OK;
+}
+
 template <typename T>
 void run_gather(const Geo& g, const void* pool_k, const void* pool_v, const float* page_kmean,
-                const int32_t* page_prompt, int cur_prompt, const void* q, int32_t* page_idx,
+                const int32_t* page_prompt, int cur_prompt, const Policy& pol, const void* q, int32_t* page_idx,
                 int32_t* n_sel, void* k_hist, void* v_hist, float* partial, float* kb, hipStream_t st) {
     launch_q_partials<T>(g, q, partial, st);
-    launch_retrieve(g, partial, page_kmean, page_prompt, cur_prompt, page_idx, n_sel, st);
+    launch_retrieve(g, partial, page_kmean, page_prompt, cur_prompt, pol.policy, pol.seed, page_idx, n_sel, st);
     if (kb)   // the history blocks of the pooled keys come with the copy
         launch_gather_pool<T>(g, pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, kb, st);
     else
@@ -245,6 +266,8 @@ HSAKV_API size_t hsakv_workspace_bytes(const hsakv_dims* dims, int32_t entry) {
         case HSAKV_ENTRY_SPARSE: return ws_sparse(g);
         case HSAKV_ENTRY_LINEAR: return ws_linear(g, eb);
         case HSAKV_ENTRY_FORWARD: return ws_forward(g, eb);
+        case HSAKV_ENTRY_SUMMARY: return align_up(page_means_ws_bytes(g, g.P));
+        case HSAKV_ENTRY_COMMIT: return align_up(page_means_ws_bytes(g, g.Lq / g.Tp + 1));
         default: return 0;
     }
 }
@@ -268,22 +291,50 @@ static int check_ws(void* ws, size_t ws_bytes, size_t need) {
 // ---- entry points ----------------------------------------------------------------
 
 HSAKV_API int hkv_page_summary(const hsakv_dims* dims, const void* pool_k, float* page_kmean,
-                               void* stream) {
+                               void* ws, size_t ws_bytes, void* stream) {
     HSAKV_CHECK(check_dims(dims));
     HSAKV_REQUIRE(pool_k && page_kmean, HSAKV_ERR_NULL_ARG);
     HSAKV_REQUIRE(aligned(pool_k) && aligned(page_kmean), HSAKV_ERR_MISALIGNED);
     const Geo g = make_geo(dims);
+    HSAKV_CHECK(check_ws(ws, ws_bytes, page_means_ws_bytes(g, g.P)));
     hipStream_t st = (hipStream_t)stream;
-    if (dims->dtype == HSAKV_BF16) launch_page_summary<bf16_t>(g, pool_k, page_kmean, st);
-    else launch_page_summary<float>(g, pool_k, page_kmean, st);
+    if (dims->dtype == HSAKV_BF16) launch_page_summary<bf16_t>(g, pool_k, page_kmean, (float*)ws, st);
+    else launch_page_summary<float>(g, pool_k, page_kmean, (float*)ws, st);
+    return done();
+}
+
+HSAKV_API int hkv_page_commit(const hsakv_dims* dims, void* pool_k, void* pool_v, float* page_kmean,
+                              int32_t* page_prompt, const void* k_chunk, const void* v_chunk, int32_t n_tokens,
+                              int64_t fill, int32_t cur_prompt, void* ws, size_t ws_bytes, void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(pool_k && pool_v && page_kmean && page_prompt && (n_tokens == 0 || (k_chunk && v_chunk)),
+                  HSAKV_ERR_NULL_ARG);
+    HSAKV_REQUIRE(aligned(pool_k) && aligned(pool_v) && aligned(page_kmean) && aligned(page_prompt, 4) &&
+                      aligned(k_chunk) && aligned(v_chunk),
+                  HSAKV_ERR_MISALIGNED);
+    const Geo g = make_geo(dims);
+    HSAKV_REQUIRE(n_tokens >= 0 && fill >= 0 && fill + (long long)n_tokens <= (long long)g.P * g.Tp,
+                  HSAKV_ERR_BAD_DIMS);
+    if (n_tokens == 0) return HSAKV_OK;
+    const int completes = (int)((fill + n_tokens) / g.Tp - fill / g.Tp);
+    if (completes > 0) HSAKV_CHECK(check_ws(ws, ws_bytes, page_means_ws_bytes(g, completes)));
+    hipStream_t st = (hipStream_t)stream;
+    if (dims->dtype == HSAKV_BF16)
+        launch_page_commit<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, k_chunk, v_chunk, n_tokens, fill,
+                                   cur_prompt, (float*)ws, st);
+    else
+        launch_page_commit<float>(g, pool_k, pool_v, page_kmean, page_prompt, k_chunk, v_chunk, n_tokens, fill,
+                                  cur_prompt, (float*)ws, st);
     return done();
 }
 
 HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void* pool_v,
                          const float* page_kmean, const int32_t* page_prompt, int32_t cur_prompt,
-                         const void* q, int32_t* page_idx, int32_t* n_sel, void* k_hist,
-                         void* v_hist, void* ws, size_t ws_bytes, void* stream) {
+                         const hsakv_retrieval* retrieval, const void* q, int32_t* page_idx,
+                         int32_t* n_sel, void* k_hist, void* v_hist, void* ws, size_t ws_bytes,
+                         void* stream) {
     HSAKV_CHECK(check_dims(dims));
+    HSAKV_CHECK(check_policy(retrieval));
     HSAKV_REQUIRE(pool_k && pool_v && page_kmean && page_prompt && q && page_idx && n_sel &&
                       k_hist && v_hist,
                   HSAKV_ERR_NULL_ARG);
@@ -295,10 +346,10 @@ HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void*
     HSAKV_CHECK(check_ws(ws, ws_bytes, ws_gather(g)));
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
-        run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, q, page_idx,
+        run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval), q, page_idx,
                            n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     else
-        run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, q, page_idx,
+        run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval), q, page_idx,
                           n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     return done();
 }
@@ -437,9 +488,12 @@ HSAKV_API int hsakv_fork_destroy(hsakv_fork* f) {
 }
 
 HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
-                          const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
-                          void* stream, const hsakv_fork* fork) {
+                          const hsakv_retrieval* retrieval, const hsakv_inputs* in,
+                          hsakv_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                          const hsakv_fork* fork) {
     HSAKV_CHECK(check_dims(dims));
+    HSAKV_CHECK(check_policy(retrieval));
+    const Policy pol = policy_of(retrieval);
     HSAKV_REQUIRE(in && out, HSAKV_ERR_NULL_ARG);
     HSAKV_CHECK(check_tau(dims, tau));
     HSAKV_REQUIRE(in->q && in->k_intra && in->v_intra && in->pool_k && in->pool_v &&
@@ -486,7 +540,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     Epi ep{out->o_sparse, out->out, o_linear, out->gate, in->w_g, in->b_g};
     hipStream_t st = (hipStream_t)stream;
     if (eb == 2) {
-        run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
+        run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol,
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         // The low-rank branch needs the gathered KV only: with a fork it runs
         // on the caller's second stream beside the pooling, the block
@@ -523,7 +577,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         launch_sparse_compute_bf16(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, sparse_ws, ep,
                                    st);
     } else {
-        run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt,
+        run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                           nullptr, qb, kb, zl, true, st);

@@ -23,10 +23,31 @@ int retrieve_slabs(const Geo&) { return kSlabs; }
 
 constexpr int kRetrieveThreads = 1024;
 
+// Output i of SplitMix64 seeded with `seed` (Steele, Lea and Flood, OOPSLA
+// 2014): the state after i + 1 steps, then the generator's output mix.
+HSAKV_DEV uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+    uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Candidate test and ranking key of each policy (HSAKV_POLICY_*): the
+// method's two-stage retrieval scores the prompt-matching pages; the
+// alternatives the pages compare it with change the candidates and the key.
+HSAKV_DEV bool policy_candidate(int policy, int prompt, int cur) {
+    switch (policy) {
+        case 0: case 2: return prompt == cur;   // two-stage, prompt-only
+        case 5: return prompt != cur;           // mismatched
+        default: return true;                   // page-only, recent, random
+    }
+}
+
 __global__ void __launch_bounds__(kRetrieveThreads)
 k_retrieve(const float* __restrict__ partial, int slabs, float inv_Lq, int HD, int P, int Kp,
            const float* __restrict__ page_kmean, const int32_t* __restrict__ page_prompt,
-           int cur_prompt, int32_t* __restrict__ page_idx, int32_t* __restrict__ n_sel) {
+           int cur_prompt, int policy, unsigned long long seed, int32_t* __restrict__ page_idx,
+           int32_t* __restrict__ n_sel) {
     extern __shared__ float smem[];
     float* qbar = smem;                       // [HD]
     float* score = smem + HD;                 // [P]
@@ -63,10 +84,27 @@ k_retrieve(const float* __restrict__ partial, int slabs, float inv_Lq, int HD, i
     // page scores, one wave per page; lanes take columns lane, lane + 64, ...
     // in a fixed order, then a fixed tree. A wave holds two pages at a time
     // (pages w and w + 16), with both pages' loads in flight together.
+    const bool by_score = policy == 0 || policy == 1 || policy == 5;
     for (int p0 = wave; p0 < P; p0 += 2 * nwaves) {
         const int p1 = p0 + nwaves;
-        const bool m0 = page_prompt[p0] == cur_prompt;
-        const bool m1 = p1 < P && page_prompt[p1] == cur_prompt;
+        const bool m0 = policy_candidate(policy, page_prompt[p0], cur_prompt);
+        const bool m1 = p1 < P && policy_candidate(policy, page_prompt[p1], cur_prompt);
+        if (!by_score) {
+            // recency (the page index) or the random key: exact in float32
+            if (lane == 0) {
+                const float k0 = policy == 4 ? (float)(splitmix64_at(seed, p0) >> 40) : (float)p0;
+                score[p0] = m0 ? k0 : 0.f;
+                cand[p0] = m0 ? 1 : 0;
+                if (m0) atomicAdd(&n_cand, 1);
+                if (p1 < P) {
+                    const float k1 = policy == 4 ? (float)(splitmix64_at(seed, p1) >> 40) : (float)p1;
+                    score[p1] = m1 ? k1 : 0.f;
+                    cand[p1] = m1 ? 1 : 0;
+                    if (m1) atomicAdd(&n_cand, 1);
+                }
+            }
+            continue;
+        }
         float s0 = 0.f, s1 = 0.f;
         int c = lane;
         const float* k0 = page_kmean + (size_t)p0 * HD;
@@ -144,11 +182,11 @@ size_t retrieve_smem_bytes(const Geo& g) {
 }
 
 void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
-                     const int32_t* page_prompt, int cur_prompt, int32_t* page_idx,
-                     int32_t* n_sel, hipStream_t st) {
+                     const int32_t* page_prompt, int cur_prompt, int policy, unsigned long long seed,
+                     int32_t* page_idx, int32_t* n_sel, hipStream_t st) {
     hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st, partial,
                        retrieve_slabs(g), 1.0f / (float)g.Lq, g.HD, g.P, g.Kp, page_kmean, page_prompt,
-                       cur_prompt, page_idx, n_sel);
+                       cur_prompt, policy, seed, page_idx, n_sel);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,89 +365,40 @@ void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* 
                        (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec);
 }
 
-// Column sums of items of consecutive token rows: item i is rows
-// [i n, min((i + 1) n, total)) of x, its sum (times `scale`) goes to out[i].
-// Used for the page summary (items = pages, scale 1/Tp) and for the slab sums
-// of the chunk-mean query. One work-group of 1024 threads per (item, 256
-// columns): 32 column lanes of 8 elements x 32 row groups, 16 rows (bf16; 8
-// for f32) in flight per thread as raw vectors. Each thread keeps a Kahan
-// sum per column over its rows (in row order); the 32 group sums are added
-// in group order, again with Kahan, so identical items give identical sums.
-template <typename T>
-__global__ void __launch_bounds__(1024)
-k_item_colsum(const T* __restrict__ x, long long rows_per_item, long long total_rows, int HD, float scale,
-              float* __restrict__ out) {
-    const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
-    const int col0 = (blockIdx.y * 32 + lane) * 8;
-    const long long item = blockIdx.x;
-    const long long r0 = item * rows_per_item;
-    const long long left = total_rows - r0;
-    const int rows = (int)(left < rows_per_item ? left : rows_per_item);
-    const T* base = x + r0 * HD + col0;
-    Kahan acc[8];
-    if (col0 < HD) {
-        constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
-        for (int t = grp; t < rows; t += 32 * kRows) {
-            Row8<T> v[kRows];
-#pragma unroll
-            for (int u = 0; u < kRows; ++u) {
-                const int tu = t + 32 * u < rows ? t + 32 * u : t;
-                v[u].load(base + (long long)tu * HD);
-            }
-#pragma unroll
-            for (int u = 0; u < kRows; ++u)
-                if (t + 32 * u < rows) {
-                    float xv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                    v[u].add_to(xv);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e].add(xv[e]);
-                }
-        }
-    }
-    __shared__ float part[32][32 * 8 + 4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[grp][lane * 8 + e] = acc[e].s;
-    __syncthreads();
-    if (threadIdx.x < 256) {
-        const int c = blockIdx.y * 256 + threadIdx.x;
-        if (c < HD) {
-            Kahan k;
-            for (int q = 0; q < 32; ++q) k.add(part[q][threadIdx.x]);
-            out[item * HD + c] = k.s * scale;
-        }
-    }
-}
+// Page means in two deterministic passes, so a page's mean does not depend on
+// which call computes it (the pool summary or the commit that completes the
+// page) and a single page still spreads over many work-groups:
+//  1. k_slab_colsum: item i (a page) is cut into kSlabs slabs of rows; the
+//     column sums of each slab go to partial[i][slab][HD];
+//  2. k_slab_mean: per item and column, the slab sums added in slab order
+//     (Kahan), times 1/rows.
 
-template <typename T>
-void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, hipStream_t st) {
-    dim3 grid(g.P, (g.HD + 255) / 256);
-    hipLaunchKernelGGL(k_item_colsum<T>, grid, dim3(1024), 0, st, (const T*)pool_k, (long long)g.Tp,
-                       (long long)g.P * g.Tp, g.HD, 1.0f / (float)g.Tp, page_kmean);
-}
-template void launch_page_summary<float>(const Geo&, const void*, float*, hipStream_t);
-template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, hipStream_t);
-
-// Slab column sums of q for the chunk mean: work-group (slab, 256 columns) of
-// 512 threads, 32 column lanes of 8 elements x 16 row groups, 16 rows (bf16;
-// 8 for f32) in flight per thread. Each thread keeps a Kahan sum per column
-// over its rows in row order; the 16 group sums are added in group order.
+// Slab column sums of `items` consecutive items of item_rows rows each:
+// work-group (item * kSlabs + slab, 256 columns) of 512 threads, 32 column
+// lanes of 8 elements x 16 row groups, 16 rows (bf16; 8 for f32) in flight
+// per thread. Each thread keeps a Kahan sum per column over its rows in row
+// order; the 16 group sums are added in group order (Kahan).
 constexpr int kQsumGroups = 16;
 
 template <typename T>
 __global__ void __launch_bounds__(32 * kQsumGroups)
-k_q_colsum(const T* __restrict__ q, int rows_per_slab, int Lq, int HD, float* __restrict__ partial) {
+k_slab_colsum(const T* __restrict__ x, long long item_rows, int HD, float* __restrict__ partial) {
     const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
     const int col0 = (blockIdx.y * 32 + lane) * 8;
-    const int r0 = blockIdx.x * rows_per_slab;
-    const int r1 = r0 + rows_per_slab < Lq ? r0 + rows_per_slab : Lq;
+    const long long item = blockIdx.x / kSlabs;
+    const int slab = blockIdx.x % kSlabs;
+    const long long per = (item_rows + kSlabs - 1) / kSlabs;
+    const long long r0 = item * item_rows + slab * per;
+    const long long end = (item + 1) * item_rows;
+    const long long r1 = r0 + per < end ? r0 + per : end;
     Kahan acc[8];
     if (col0 < HD) {
         constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
-        for (int t = r0 + grp; t < r1; t += kQsumGroups * kRows) {
+        for (long long t = r0 + grp; t < r1; t += kQsumGroups * kRows) {
             Row8<T> v[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u)
-                if (t + kQsumGroups * u < r1) v[u].load(q + (long long)(t + kQsumGroups * u) * HD + col0);
+                if (t + kQsumGroups * u < r1) v[u].load(x + (t + kQsumGroups * u) * HD + col0);
 #pragma unroll
             for (int u = 0; u < kRows; ++u)
                 if (t + kQsumGroups * u < r1) {
@@ -433,12 +422,105 @@ k_q_colsum(const T* __restrict__ q, int rows_per_slab, int Lq, int HD, float* __
     }
 }
 
+// out[item][c] = (sum over slabs, in slab order, of partial[item][slab][c]) * scale
+__global__ void __launch_bounds__(256)
+k_slab_mean(const float* __restrict__ partial, int HD, float scale, float* __restrict__ out) {
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= HD) return;
+    const long long item = blockIdx.x;
+    float v[kSlabs];
+#pragma unroll
+    for (int k = 0; k < kSlabs; ++k) v[k] = partial[(size_t)(item * kSlabs + k) * HD + c];
+    Kahan s;
+#pragma unroll
+    for (int k = 0; k < kSlabs; ++k) s.add(v[k]);
+    out[item * HD + c] = s.s * scale;
+}
+
+// Page means of `count` pages starting at `pages` into page_kmean rows
+// starting at `kmean`; partial holds count * kSlabs * HD floats.
+template <typename T>
+void launch_page_means(const Geo& g, const T* pages, int count, float* kmean, float* partial, hipStream_t st) {
+    dim3 g1((unsigned)count * kSlabs, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_slab_colsum<T>, g1, dim3(32 * kQsumGroups), 0, st, pages, (long long)g.Tp, g.HD, partial);
+    dim3 g2((unsigned)count, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_slab_mean, g2, dim3(256), 0, st, (const float*)partial, g.HD, 1.0f / (float)g.Tp, kmean);
+}
+
+size_t page_means_ws_bytes(const Geo& g, int pages) { return (size_t)pages * kSlabs * g.HD * 4; }
+
+template <typename T>
+void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, float* partial, hipStream_t st) {
+    launch_page_means<T>(g, (const T*)pool_k, g.P, page_kmean, partial, st);
+}
+template void launch_page_summary<float>(const Geo&, const void*, float*, float*, hipStream_t);
+template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, float*, hipStream_t);
+
+// Slab column sums of q for the chunk mean: q is one item of Lq rows.
 template <typename T>
 void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
-    const int slabs = retrieve_slabs(g);
-    const int per = (g.Lq + slabs - 1) / slabs;
-    dim3 grid(slabs, (g.HD + 255) / 256);
-    hipLaunchKernelGGL(k_q_colsum<T>, grid, dim3(32 * kQsumGroups), 0, st, (const T*)q, per, g.Lq, g.HD, partial);
+    dim3 grid(kSlabs, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_slab_colsum<T>, grid, dim3(32 * kQsumGroups), 0, st, (const T*)q, (long long)g.Lq, g.HD,
+                       partial);
 }
 template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
 template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Page commit: the chunk's K and V rows become history tokens [fill, fill + n)
+// of the pool (pages are consecutive in the pool, so that is one contiguous
+// row range), then each page the commit completes gets its page-mean key
+// (the page summary kernel, per page) and the committing prompt's id.
+
+__global__ void __launch_bounds__(kGatherThreads)
+k_commit_copy(const u32x4* __restrict__ k_chunk, const u32x4* __restrict__ v_chunk, u32x4* __restrict__ pool_k,
+              u32x4* __restrict__ pool_v, long long vec, long long dst_off) {
+    const u32x4* src = blockIdx.y == 0 ? k_chunk : v_chunk;
+    u32x4* dst = (blockIdx.y == 0 ? pool_k : pool_v) + dst_off;
+    const long long chunk = (long long)kGatherThreads * kGatherUnroll;
+    for (long long base = (long long)blockIdx.x * chunk; base < vec; base += (long long)gridDim.x * chunk) {
+        u32x4 v[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const long long i = base + u * kGatherThreads + threadIdx.x;
+            if (i < vec) v[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const long long i = base + u * kGatherThreads + threadIdx.x;
+            if (i < vec) dst[i] = v[u];
+        }
+    }
+}
+
+__global__ void k_tag_pages(int32_t* __restrict__ page_prompt, int first, int count, int32_t tag) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) page_prompt[first + i] = tag;
+}
+
+template <typename T>
+void launch_page_commit(const Geo& g, void* pool_k, void* pool_v, float* page_kmean, int32_t* page_prompt,
+                        const void* k_chunk, const void* v_chunk, int n, long long fill, int cur_prompt,
+                        float* partial, hipStream_t st) {
+    const long long vec = (long long)n * g.HD * (long long)sizeof(T) / 16;
+    const long long chunk = (long long)kGatherThreads * kGatherUnroll;
+    long long blocks = (vec + chunk - 1) / chunk;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks > 0)
+        hipLaunchKernelGGL(k_commit_copy, dim3((unsigned)blocks, 2), dim3(kGatherThreads), 0, st,
+                           (const u32x4*)k_chunk, (const u32x4*)v_chunk, (u32x4*)pool_k, (u32x4*)pool_v, vec,
+                           fill * g.HD * (long long)sizeof(T) / 16);
+    // pages p with fill < (p + 1) Tp <= fill + n
+    const long long first = fill / g.Tp, last = (fill + n) / g.Tp;   // [first, last)
+    const int count = (int)(last - first);
+    if (count > 0) {
+        const T* pages = (const T*)pool_k + first * (long long)g.Tp * g.HD;
+        launch_page_means<T>(g, pages, count, page_kmean + first * g.HD, partial, st);
+        hipLaunchKernelGGL(k_tag_pages, dim3((count + 255) / 256), dim3(256), 0, st, page_prompt, (int)first, count,
+                           (int32_t)cur_prompt);
+    }
+}
+template void launch_page_commit<float>(const Geo&, void*, void*, float*, int32_t*, const void*, const void*, int,
+                                        long long, int, float*, hipStream_t);
+template void launch_page_commit<bf16_t>(const Geo&, void*, void*, float*, int32_t*, const void*, const void*, int,
+                                         long long, int, float*, hipStream_t);

@@ -23,12 +23,21 @@ struct Epi {
     const float* b_g;
 };
 
-template <typename T> void launch_page_summary(const Geo&, const void* pool_k, float* page_kmean, hipStream_t);
+// Page means: partial holds page_means_ws_bytes(g, pages) bytes of scratch.
+size_t page_means_ws_bytes(const Geo&, int pages);
+template <typename T>
+void launch_page_summary(const Geo&, const void* pool_k, float* page_kmean, float* partial, hipStream_t);
+// Page commit: chunk rows -> pool rows [fill, fill + n); page means and tags of the pages completed.
+template <typename T>
+void launch_page_commit(const Geo&, void* pool_k, void* pool_v, float* page_kmean, int32_t* page_prompt,
+                        const void* k_chunk, const void* v_chunk, int n, long long fill, int cur_prompt,
+                        float* partial, hipStream_t);
 int retrieve_slabs(const Geo&);
 size_t retrieve_smem_bytes(const Geo&);
 template <typename T> void launch_q_partials(const Geo&, const void* q, float* partial, hipStream_t);
 void launch_retrieve(const Geo&, const float* partial, const float* page_kmean, const int32_t* page_prompt,
-                     int cur_prompt, int32_t* page_idx, int32_t* n_sel, hipStream_t);
+                     int cur_prompt, int policy, unsigned long long seed, int32_t* page_idx, int32_t* n_sel,
+                     hipStream_t);
 void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* pool_v, const int32_t* page_idx,
                    const int32_t* n_sel, void* k_hist, void* v_hist, hipStream_t);
 // The gather with the history blocks of the pooled keys kb written on the way.

@@ -47,12 +47,14 @@ ENTRY_SELECT = 2
 ENTRY_SPARSE = 3
 ENTRY_LINEAR = 4
 ENTRY_FORWARD = 6
+ENTRY_SUMMARY = 7
+ENTRY_COMMIT = 8
 
 EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
     "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
-    "hsa_sparse_attn_static",
+    "hsa_sparse_attn_static", "hkv_page_commit",
 ]
 
 
@@ -94,6 +96,21 @@ class Outputs(ctypes.Structure):
         "o_linear", "gate")]
 
 
+POLICIES = {"two_stage": 0, "page_only": 1, "prompt_only": 2, "recent": 3, "random": 4, "mismatched": 5}
+
+
+class Retrieval(ctypes.Structure):
+    """hsakv_retrieval: retrieval policy and the seed of the random policy."""
+    _fields_ = [("policy", c_int32), ("reserved", c_int32), ("seed", ctypes.c_uint64)]
+
+
+def _retrieval(policy, seed):
+    if policy is None:
+        return None
+    pid = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    return ctypes.byref(Retrieval(pid, 0, int(seed)))
+
+
 class Fork(ctypes.Structure):
     """hsakv_fork: a caller-owned second stream and two events (hipStream_t,
     hipEvent_t handles) for hsa_forward's low-rank branch."""
@@ -108,15 +125,18 @@ _sig = {
     "hsakv_last_hip_error": (c_int32, []),
     "hsakv_validate": (c_int32, [_D]),
     "hsakv_workspace_bytes": (c_size_t, [_D, c_int32]),
-    "hkv_page_summary": (c_int32, [_D, _P, _P, _P]),
-    "hkv_gather": (c_int32, [_D, _P, _P, _P, _P, c_int32, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
+    "hkv_page_summary": (c_int32, [_D, _P, _P, _P, c_size_t, _P]),
+    "hkv_gather": (c_int32, [_D, _P, _P, _P, _P, c_int32, ctypes.POINTER(Retrieval), _P, _P, _P, _P, _P, _P,
+                             c_size_t, _P]),
     "hsa_select": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_sparse_attn": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_linear_branch": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_fuse": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Inputs), ctypes.POINTER(Outputs), _P,
-                              c_size_t, _P, ctypes.POINTER(Fork)]),
+    "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Retrieval), ctypes.POINTER(Inputs),
+                              ctypes.POINTER(Outputs), _P, c_size_t, _P, ctypes.POINTER(Fork)]),
     "hsa_sparse_attn_static": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hkv_page_commit": (c_int32, [_D, _P, _P, _P, _P, _P, _P, c_int32, ctypes.c_int64, c_int32, _P, c_size_t,
+                                  _P]),
     "hsakv_fork_create": (c_int32, [ctypes.POINTER(Fork)]),
     "hsakv_fork_destroy": (c_int32, [ctypes.POINTER(Fork)]),
 }
@@ -162,6 +182,16 @@ def _host_f32(x) -> ctypes.Array:
     return (ctypes.c_float * len(vals))(*vals)
 
 
+def _scratch(nbytes: int, like):
+    """A device byte buffer for a workspace, on the device of tensor `like`
+    (None when `like` is not a tensor: the library then rejects the call on
+    the host)."""
+    if not hasattr(like, "device") or nbytes <= 0:
+        return None
+    import torch
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+
+
 def _ws(ws):
     if ws is None:
         return None, 0
@@ -193,18 +223,36 @@ def make_dims(*, H, d, Lq, tokens_per_frame, Psize, P, Kp, Binter, Bintra, Bq, r
 
 # ---- entry points ------------------------------------------------------------
 
-def hkv_page_summary(dims: Dims, pool_k, page_kmean, stream=None) -> None:
+def hkv_page_summary(dims: Dims, pool_k, page_kmean, ws=None, stream=None) -> None:
+    """ws: a device buffer of workspace_bytes(dims, ENTRY_SUMMARY) bytes (allocated
+    here through torch when None)."""
+    if ws is None:
+        ws = _scratch(workspace_bytes(dims, ENTRY_SUMMARY), page_kmean)
+    w, wb = _ws(ws)
     _check("hkv_page_summary", _lib.hkv_page_summary(
-        ctypes.byref(dims), _ptr(pool_k), _ptr(page_kmean), _stream(stream)))
+        ctypes.byref(dims), _ptr(pool_k), _ptr(page_kmean), w, wb, _stream(stream)))
+
+
+def hkv_page_commit(dims: Dims, pool_k, pool_v, page_kmean, page_prompt, k_chunk, v_chunk,
+                    n_tokens: int, fill: int, cur_prompt: int, ws=None, stream=None) -> None:
+    """ws: a device buffer of workspace_bytes(dims, ENTRY_COMMIT) bytes (allocated
+    here through torch when None)."""
+    if ws is None:
+        ws = _scratch(workspace_bytes(dims, ENTRY_COMMIT), page_kmean)
+    w, wb = _ws(ws)
+    _check("hkv_page_commit", _lib.hkv_page_commit(
+        ctypes.byref(dims), _ptr(pool_k), _ptr(pool_v), _ptr(page_kmean), _ptr(page_prompt),
+        _ptr(k_chunk), _ptr(v_chunk), int(n_tokens), int(fill), int(cur_prompt), w, wb,
+        _stream(stream)))
 
 
 def hkv_gather(dims: Dims, pool_k, pool_v, page_kmean, page_prompt, cur_prompt: int, q, page_idx,
-               n_sel, k_hist, v_hist, ws, stream=None) -> None:
+               n_sel, k_hist, v_hist, ws, stream=None, policy=None, seed: int = 0) -> None:
     w, wb = _ws(ws)
     _check("hkv_gather", _lib.hkv_gather(
         ctypes.byref(dims), _ptr(pool_k), _ptr(pool_v), _ptr(page_kmean), _ptr(page_prompt),
-        int(cur_prompt), _ptr(q), _ptr(page_idx), _ptr(n_sel), _ptr(k_hist), _ptr(v_hist), w, wb,
-        _stream(stream)))
+        int(cur_prompt), _retrieval(policy, seed), _ptr(q), _ptr(page_idx), _ptr(n_sel), _ptr(k_hist),
+        _ptr(v_hist), w, wb, _stream(stream)))
 
 
 def hsa_select(dims: Dims, q, k_hist, k_intra, n_sel, tau, sel_count, sel_idx, sel_mask=None,
@@ -260,11 +308,11 @@ def fork_destroy(f: Fork) -> None:
 
 
 def hsa_forward(dims: Dims, tau, cur_prompt: int, inputs: dict, outputs: dict, ws,
-                stream=None, fork: Optional[Fork] = None) -> None:
+                stream=None, fork: Optional[Fork] = None, policy=None, seed: int = 0) -> None:
     ins = Inputs(*[_ptr(inputs.get(n)) for n, _ in Inputs._fields_])
     outs = Outputs(*[_ptr(outputs.get(n)) for n, _ in Outputs._fields_])
     w, wb = _ws(ws)
     _check("hsa_forward", _lib.hsa_forward(
         ctypes.byref(dims), ctypes.cast(_host_f32(tau), c_void_p), int(cur_prompt),
-        ctypes.byref(ins), ctypes.byref(outs), w, wb, _stream(stream),
+        _retrieval(policy, seed), ctypes.byref(ins), ctypes.byref(outs), w, wb, _stream(stream),
         ctypes.byref(fork) if fork is not None else None))

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HSAKV_VERSION 2
+#define HSAKV_VERSION 3
 
 /* status codes */
 #define HSAKV_OK                   0
@@ -95,6 +95,8 @@ extern "C" {
 #define HSAKV_ENTRY_SPARSE   3
 #define HSAKV_ENTRY_LINEAR   4
 #define HSAKV_ENTRY_FORWARD  6
+#define HSAKV_ENTRY_SUMMARY  7
+#define HSAKV_ENTRY_COMMIT   8   /* enough for a commit of up to Lq tokens */
 
 /* Sizes of one chunk-layer; all host integers. Supported: d in {64, 128};
  * Bq = 64; Binter and Bintra multiples of 64 up to 512; r a multiple of 32
@@ -116,6 +118,33 @@ typedef struct hsakv_dims {
     int32_t r;                /* Linformer rank */
     int32_t dtype;            /* HSAKV_F32 or HSAKV_BF16 */
 } hsakv_dims;
+
+/* Retrieval policies. TWO_STAGE is the method (prompt-level filter, then the
+ * top-Kp pages by page score); the others are the alternatives the pages
+ * compare it with under the same page budget (HKV paragraph, Table 6;
+ * Table 5's sliding window of recent frames is RECENT). Each keeps Kp
+ * pages (fewer if fewer are candidates), ties to the lower page, slots in
+ * ascending page order:
+ *   PAGE_ONLY    every page, by page score
+ *   PROMPT_ONLY  the Kp most recent (highest-index) prompt-matching pages
+ *   RECENT       the Kp most recent pages
+ *   RANDOM       every page, by the top 24 bits of output p of SplitMix64
+ *                seeded with `seed` (Steele, Lea and Flood, OOPSLA 2014)
+ *   MISMATCHED   the pages of other prompts, by page score */
+#define HSAKV_POLICY_TWO_STAGE    0
+#define HSAKV_POLICY_PAGE_ONLY    1
+#define HSAKV_POLICY_PROMPT_ONLY  2
+#define HSAKV_POLICY_RECENT       3
+#define HSAKV_POLICY_RANDOM       4
+#define HSAKV_POLICY_MISMATCHED   5
+
+/* Retrieval options (host struct; NULL means TWO_STAGE). A policy outside
+ * 0..5 returns HSAKV_ERR_UNSUPPORTED. */
+typedef struct hsakv_retrieval {
+    int32_t  policy;
+    int32_t  reserved;   /* set to 0 */
+    uint64_t seed;       /* RANDOM only */
+} hsakv_retrieval;
 
 /* Inputs of the fused forward; every pointer is device memory. */
 typedef struct hsakv_inputs {
@@ -189,9 +218,34 @@ int hsakv_fork_destroy(hsakv_fork* fork);
  * pool_k[p][:][h][:]. Commit-time metadata of each semantic page (HKV
  * paragraph: semantically indexed pages; the score that uses it is the
  * page-level retrieval stage). Reads pool_k (device), writes page_kmean
- * (device, f32 [P][H][d]). Float32 accumulation in a fixed order, so
- * identical pages give identical means. */
-int hkv_page_summary(const hsakv_dims* dims, const void* pool_k, float* page_kmean, void* stream);
+ * (device, f32 [P][H][d]). Float32 accumulation in a fixed order (each page
+ * in 32 row slabs, then the slab sums in slab order), so identical pages
+ * give identical means, and a page's mean is the same bits as the one
+ * hkv_page_commit gives it. Workspace: HSAKV_ENTRY_SUMMARY. */
+int hkv_page_summary(const hsakv_dims* dims, const void* pool_k, float* page_kmean, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Page commit (HKV paragraph: the history's KV pairs are cut into semantic
+ * pages of Psize frames, indexed for the prompt-level and page-level
+ * retrieval stages; project page, second caption). The history is one token
+ * sequence; page p of the pool holds its tokens [p*Tp, (p+1)*Tp), and
+ * `fill` (host) tokens are already committed. The chunk's n_tokens rows of
+ * k_chunk, v_chunk (device, [n_tokens][H][d] dtype) become history tokens
+ * [fill, fill + n_tokens): pool rows, since pages are consecutive. Every
+ * page the commit completes (fill < (p+1)*Tp <= fill + n_tokens) is
+ * finalised: page_kmean[p] (device f32 [P][H][d]) is its page-mean key,
+ * computed exactly as hkv_page_summary does, and page_prompt[p] (device
+ * int32 [P]) is set to cur_prompt (host). Other pages' means and tags are
+ * untouched. Only finalised pages should be offered to retrieval: pass
+ * dims->P = (fill + n_tokens) / Tp finalised pages to hkv_gather and
+ * hsa_forward. dims->P here is the pool's capacity in pages; fill +
+ * n_tokens beyond P*Tp returns HSAKV_ERR_BAD_DIMS. n_tokens = 0 does
+ * nothing. Workspace: HSAKV_ENTRY_COMMIT covers commits of up to dims->Lq
+ * tokens; a commit completing c pages needs c * 32 * H * d * 4 bytes (none
+ * when it completes no page). */
+int hkv_page_commit(const hsakv_dims* dims, void* pool_k, void* pool_v, float* page_kmean,
+                    int32_t* page_prompt, const void* k_chunk, const void* v_chunk, int32_t n_tokens,
+                    int64_t fill, int32_t cur_prompt, void* ws, size_t ws_bytes, void* stream);
 
 /* Two-stage retrieval and active-cache assembly (HKV paragraph: prompt-level
  * then page-level top-Kp; kernel paragraph: contiguous copies).
@@ -204,12 +258,14 @@ int hkv_page_summary(const hsakv_dims* dims, const void* pool_k, float* page_kme
  *     set to -1) and *n_sel (device).
  *  3. Gather: k_hist[s*Tp + t] = pool_k[page_idx[s]][t] for s < n_sel, same
  *     for v; a bit copy. Rows at or past n_sel*Tp are not written.
- * q is [Lq][H][d] (device). cur_prompt is a host value. Workspace:
- * HSAKV_ENTRY_GATHER. */
+ * q is [Lq][H][d] (device). cur_prompt is a host value. `retrieval` (host,
+ * nullable) selects another policy for steps 1-2 (see hsakv_retrieval).
+ * Workspace: HSAKV_ENTRY_GATHER. */
 int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void* pool_v,
                const float* page_kmean, const int32_t* page_prompt, int32_t cur_prompt,
-               const void* q, int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist,
-               void* ws, size_t ws_bytes, void* stream);
+               const hsakv_retrieval* retrieval, const void* q, int32_t* page_idx,
+               int32_t* n_sel, void* k_hist, void* v_hist, void* ws, size_t ws_bytes,
+               void* stream);
 
 /* Head-adaptive block selection (HSA paragraph: per head, the fewest blocks
  * whose cumulative attention mass reaches tau_h; Binter history blocks,
@@ -285,16 +341,17 @@ int hsa_fuse(const hsakv_dims* dims, const void* q, const float* w_g, const floa
 /* The whole chunk-layer: retrieval and gather, selection, linear branch,
  * sparse attention and the gate, with the gate fused into the sparse
  * attention's epilogue. Results equal the separate entry points run in that
- * order. tau (host, H floats) and cur_prompt (host) as above. Workspace:
- * HSAKV_ENTRY_FORWARD.
+ * order. tau (host, H floats), cur_prompt (host) and retrieval (host,
+ * nullable) as above. Workspace: HSAKV_ENTRY_FORWARD.
  * `fork` (host, nullable): with a fork whose stream is set and bf16 data, the
  * low-rank branch runs on the fork's stream beside the selection (see
  * hsakv_fork); NULL, or a fork with a NULL stream, runs everything on
  * `stream`. The results are the same either way. float32 data always runs on
  * `stream`. */
 int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
-                const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
-                void* stream, const hsakv_fork* fork);
+                const hsakv_retrieval* retrieval, const hsakv_inputs* in,
+                hsakv_outputs* out, void* ws, size_t ws_bytes, void* stream,
+                const hsakv_fork* fork);
 
 #ifdef __cplusplus
 }

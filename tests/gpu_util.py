@@ -119,6 +119,21 @@ def masked_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, ids, blocks) -
     return torch.nn.functional.scaled_dot_product_attention(t(q), t(K[J]), t(V[J]))[0, 0].numpy()
 
 
+def expected_sparse(s, ch, ref, cnt, idx, differ) -> np.ndarray:
+    """The oracle's O_s, with each boundary row (h, i) in `differ` replaced by
+    the library check of attention over the GPU's own (valid) set."""
+    want = ref["o_sparse"].copy()
+    if differ:
+        q = oracle.as_f64(ch["q"], s.dtype)
+        K = np.concatenate([oracle.as_f64(ref["k_hist"], s.dtype), oracle.as_f64(ch["k_intra"], s.dtype)])
+        V = np.concatenate([oracle.as_f64(ref["v_hist"], s.dtype), oracle.as_f64(ch["v_intra"], s.dtype)])
+        for (h, i) in differ:
+            q0, q1 = ref["qblocks"][i]
+            want[q0:q1, h] = masked_attention(q[q0:q1, h], K[:, h], V[:, h], idx[h, i, :cnt[h, i]].tolist(),
+                                              ref["blocks"])
+    return want
+
+
 def pack_selection(sel, NB_max: int):
     """Oracle selection lists -> (sel_count [H][NQB], sel_idx [H][NQB][NB_max]) int32."""
     H, NQB = len(sel), len(sel[0])
@@ -166,7 +181,7 @@ class Case:
         self.t["pool_v"] = dev(self.pool_v)
 
     # -- oracle ---------------------------------------------------------------
-    def oracle(self, **kw) -> dict:
+    def oracle(self, **kw) -> dict:  # noqa: D401 - keyword arguments go to oracle.forward
         s, ch = self.s, self.ch
         return oracle.forward(
             dtype=s.dtype, q=ch["q"], k_intra=ch["k_intra"], v_intra=ch["v_intra"],
@@ -181,7 +196,7 @@ class Case:
         hs.hkv_page_summary(self.d, self.t["pool_k"], km)
         return km
 
-    def gather(self, page_kmean: torch.Tensor):
+    def gather(self, page_kmean: torch.Tensor, policy=None, seed=0):
         s, d = self.s, self.d
         page_idx = torch.full((s.Kp,), -7, dtype=torch.int32, device="cuda")
         n_sel = torch.full((1,), -7, dtype=torch.int32, device="cuda")
@@ -189,7 +204,7 @@ class Case:
         v_hist = torch.zeros_like(k_hist)
         hs.hkv_gather(d, self.t["pool_k"], self.t["pool_v"], page_kmean, self.t["page_prompt"],
                       self.cur_prompt, self.t["q"], page_idx, n_sel, k_hist, v_hist,
-                      ws(d, hs.ENTRY_GATHER))
+                      ws(d, hs.ENTRY_GATHER), policy=policy, seed=seed)
         return page_idx, n_sel, k_hist, v_hist
 
     def select(self, k_hist, n_sel, tau=None):
@@ -226,7 +241,7 @@ class Case:
         hs.hsa_fuse(d, self.t["q"], self.t["w_g"], self.t["b_g"], o_s, o_l, out, gate)
         return out, gate
 
-    def forward(self, page_kmean, debug=True, fork="default"):
+    def forward(self, page_kmean, debug=True, fork="default", policy=None, seed=0):
         s, d = self.s, self.d
         outs = {"out": torch.zeros((s.Lq, s.H, s.d), dtype=tdtype(s), device="cuda")}
         if debug:
@@ -247,5 +262,5 @@ class Case:
         if fork == "default":
             fork = default_fork()
         hs.hsa_forward(d, self.ch["tau"], self.cur_prompt, ins, outs, ws(d, hs.ENTRY_FORWARD),
-                       fork=fork)
+                       fork=fork, policy=policy, seed=seed)
         return outs

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from block_sparse_rank_amd import hsakv as hs  # noqa: E402
-from gpu_util import (Case, check_selection, compare, dev, host, masked_attention,  # noqa: E402
+from gpu_util import (Case, check_selection, compare, dev, expected_sparse, host,  # noqa: E402
                       pack_selection)
 
 
@@ -165,15 +165,7 @@ def test_forward_end_to_end(case):
     print(f"rows at the boundary: {len(differ)} of {s.H * len(ref['qblocks'])}")
     # a row whose (valid) set differs at the boundary is checked against
     # attention over its own set; every other row against the oracle
-    want_s = ref["o_sparse"].copy()
-    if differ:
-        q = oracle.as_f64(case.ch["q"], s.dtype)
-        K = np.concatenate([oracle.as_f64(ref["k_hist"], s.dtype), oracle.as_f64(case.ch["k_intra"], s.dtype)])
-        V = np.concatenate([oracle.as_f64(ref["v_hist"], s.dtype), oracle.as_f64(case.ch["v_intra"], s.dtype)])
-        for (h, i) in differ:
-            q0, q1 = ref["qblocks"][i]
-            want_s[q0:q1, h] = masked_attention(q[q0:q1, h], K[:, h], V[:, h], idx[h, i, :cnt[h, i]].tolist(),
-                                                ref["blocks"])
+    want_s = expected_sparse(s, case.ch, ref, cnt, idx, differ)
     compare("o_linear(fwd)", host(outs["o_linear"]), ref["o_linear"], s.dtype)
     compare("o_sparse(fwd)", host(outs["o_sparse"]), want_s, s.dtype)
     compare("gate(fwd)", host(outs["gate"]), ref["gate"], "f32", max_abs=1e-6, rel=1e-6)
@@ -363,6 +355,41 @@ def test_nan_page_scores_rank_last():
         pi = host(page_idx)
         assert pi[:n].tolist() == want.tolist(), (Kp, pi, want)
         assert np.all(pi[n:] == -1)
+
+
+@pytest.mark.parametrize("policy", ["two_stage", "page_only", "prompt_only", "recent", "random",
+                                    "mismatched"])
+@pytest.mark.parametrize("Kp,seed", [(4, 0), (3, 987654321)])
+def test_retrieval_policies(policy, Kp, seed):
+    """Every retrieval policy on a 12-page pool with three prompts: the pages
+    chosen and the gathered rows equal the oracle's."""
+    s = synth.shape("tiny").with_(P=12, Kp=Kp, seed=34)
+    prompts = np.array([p % 3 for p in range(12)], np.int32)
+    c = Case(s, page_prompt=prompts, cur_prompt=1)
+    km = c.page_summary()
+    kmh = host(km).astype(np.float64)
+    qbar = oracle.chunk_query_mean(oracle.as_f64(c.ch["q"], s.dtype))
+    want, n = oracle.retrieve(kmh, prompts, 1, qbar, Kp, policy, seed)
+    page_idx, n_sel, k_hist, _ = c.gather(km, policy=policy, seed=seed)
+    assert int(host(n_sel)[0]) == n
+    assert host(page_idx)[:n].tolist() == want.tolist(), (policy, host(page_idx), want)
+    assert host(k_hist)[:n * s.Tp].tobytes() == np.concatenate([c.pool_k[p] for p in want]).tobytes()
+
+
+@pytest.mark.parametrize("policy", ["recent", "random", "mismatched"])
+def test_forward_with_other_policies(policy):
+    s = synth.shape("tiny").with_(dtype="bf16", P=10, Kp=3, clustered=True, tau_law="uniform", seed=35)
+    prompts = np.array([p % 2 for p in range(10)], np.int32)
+    c = Case(s, page_prompt=prompts)
+    ref = c.oracle(policy=policy, seed=77)
+    outs = c.forward(c.page_summary(), policy=policy, seed=77)
+    n = int(host(outs["n_sel"])[0])
+    assert n == ref["n_sel"] and host(outs["page_idx"])[:n].tolist() == ref["page_idx"].tolist()
+    cnt, idx = host(outs["sel_count"]), host(outs["sel_idx"])
+    differ = check_selection(cnt, idx, ref["mass"], ref["sel"], [float(t) for t in c.ch["tau"]])
+    want_s = expected_sparse(s, c.ch, ref, cnt, idx, differ)
+    compare(f"out({policy})", oracle.as_f64(host(outs["out"]), s.dtype),
+            oracle.fuse(ref["gate"], want_s, ref["o_linear"]), s.dtype)
 
 
 def test_gate_limits_isolate_branches():

@@ -38,7 +38,7 @@ def test_header_declares_exactly_the_exports():
 
 
 def test_version_and_status_strings():
-    assert hs.version() == 2
+    assert hs.version() == 3
     for code in range(-9, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
@@ -54,7 +54,8 @@ def test_workloads_validate(name):
                      P=s.P, Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r,
                      dtype=s.dtype)
     assert hs.validate(d) == hs.OK
-    for e in (hs.ENTRY_GATHER, hs.ENTRY_SELECT, hs.ENTRY_SPARSE, hs.ENTRY_LINEAR, hs.ENTRY_FORWARD):
+    for e in (hs.ENTRY_GATHER, hs.ENTRY_SELECT, hs.ENTRY_SPARSE, hs.ENTRY_LINEAR, hs.ENTRY_FORWARD,
+              hs.ENTRY_SUMMARY, hs.ENTRY_COMMIT):
         assert hs.workspace_bytes(d, e) > 0
         assert hs.workspace_bytes(d, e) % 256 == 0
     assert hs.workspace_bytes(d, 99) == 0
@@ -110,6 +111,32 @@ def test_static_sparse_rejects_what_exceeds_its_scratch():
     assert hs._lib.hsakv_last_hip_error() == 0
 
 
+def test_page_commit_rejects_before_launch():
+    d = _dims(P=2)
+    Tp = d.Tp
+    _expect(hs.ERR_BAD_DIMS, hs.hkv_page_commit, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2 * Tp - 5, 0,
+            stream=0)
+    _expect(hs.ERR_BAD_DIMS, hs.hkv_page_commit, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 0, 0, stream=0)
+    _expect(hs.ERR_BAD_DIMS, hs.hkv_page_commit, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, -3, 0, stream=0)
+    _expect(hs.ERR_NULL_ARG, hs.hkv_page_commit, d, FAKE, FAKE, FAKE, FAKE, None, FAKE, 10, 0, 0, stream=0)
+    _expect(hs.ERR_MISALIGNED, hs.hkv_page_commit, d, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 10, 0, 0,
+            stream=0)
+    # nothing to commit: returns at once, nothing enqueued
+    assert hs._lib.hkv_page_commit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, 0, 5, 0, None, 0,
+                                   None) == 0
+    # a commit that completes a page needs the page-mean scratch
+    need = hs.workspace_bytes(d, hs.ENTRY_COMMIT)
+    assert need >= 32 * d.H * d.d * 4
+    for ws_ptr, nbytes in ((None, 0), (FAKE, 32 * d.H * d.d * 4 - 1), (FAKE + 16, need)):
+        st = hs._lib.hkv_page_commit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, Tp - 50, 0,
+                                     ws_ptr, nbytes, None)
+        assert st == hs.ERR_WORKSPACE
+    st = hs._lib.hkv_page_summary(ctypes.byref(d), FAKE, FAKE, FAKE, hs.workspace_bytes(d, hs.ENTRY_SUMMARY) - 1,
+                                  None)
+    assert st == hs.ERR_WORKSPACE
+    assert hs._lib.hsakv_last_hip_error() == 0
+
+
 def test_null_dims():
     assert hs._lib.hsakv_validate(None) == hs.ERR_NULL_ARG
 
@@ -139,14 +166,14 @@ def test_entry_points_reject_before_launch():
         _expect(hs.ERR_BAD_TAU, hs.hsa_select, d, FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE,
                 stream=0)
     # workspace missing, too small, misaligned
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, None, 0, None)
     assert st == hs.ERR_WORKSPACE
     need = hs.workspace_bytes(d, hs.ENTRY_GATHER)
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE, need - 1, None)
     assert st == hs.ERR_WORKSPACE
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE + 16, need, None)
     assert st == hs.ERR_WORKSPACE
     # forward: null struct members
@@ -162,9 +189,14 @@ def test_entry_points_reject_before_launch():
     need = hs.workspace_bytes(d, hs.ENTRY_FORWARD)
     for ws_ptr, nbytes in ((FAKE, need - 1), (FAKE + 16, need), (None, need)):
         st = hs._lib.hsa_forward(ctypes.byref(d), ctypes.cast(hs._host_f32([0.5] * H), ctypes.c_void_p),
-                                 0, ctypes.byref(hs.Inputs(*[FAKE] * len(hs.Inputs._fields_))),
+                                 0, None, ctypes.byref(hs.Inputs(*[FAKE] * len(hs.Inputs._fields_))),
                                  ctypes.byref(hs.Outputs(FAKE)), ws_ptr, nbytes, None, None)
         assert st == hs.ERR_WORKSPACE
+    # an unknown retrieval policy
+    _expect(hs.ERR_UNSUPPORTED, hs.hsa_forward, d, [0.5] * H, 0, full, {"out": FAKE}, None, stream=0,
+            policy=9)
+    _expect(hs.ERR_UNSUPPORTED, hs.hkv_gather, d, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+            None, stream=0, policy=-1)
     # no launch happened, so no HIP error was recorded
     assert hs._lib.hsakv_last_hip_error() == 0
 
