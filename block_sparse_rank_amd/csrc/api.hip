@@ -408,6 +408,35 @@ HSAKV_API int hsa_sparse_attn(const hsakv_dims* dims, const void* q, const void*
     return done();
 }
 
+HSAKV_API int hsa_sparse_plan(const hsakv_dims* dims, const int32_t* n_sel, const int32_t* sel_count,
+                              const int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(dims->dtype == HSAKV_BF16, HSAKV_ERR_BAD_DTYPE);
+    HSAKV_REQUIRE(n_sel && sel_count && sel_idx, HSAKV_ERR_NULL_ARG);
+    HSAKV_REQUIRE(aligned(n_sel, 4) && aligned(sel_count, 4) && aligned(sel_idx, 4), HSAKV_ERR_MISALIGNED);
+    const Geo g = make_geo(dims);
+    HSAKV_CHECK(check_ws(ws, ws_bytes, ws_sparse(g)));
+    launch_sparse_plan_bf16(g, n_sel, sel_count, sel_idx, ws, (hipStream_t)stream);
+    return done();
+}
+
+HSAKV_API int hsa_sparse_compute(const hsakv_dims* dims, const void* q, const void* k_hist,
+                                 const void* v_hist, const void* k_intra, const void* v_intra,
+                                 const int32_t* n_sel, float* o_sparse, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(dims->dtype == HSAKV_BF16, HSAKV_ERR_BAD_DTYPE);
+    HSAKV_REQUIRE(q && k_hist && v_hist && k_intra && v_intra && n_sel && o_sparse, HSAKV_ERR_NULL_ARG);
+    HSAKV_REQUIRE(aligned(q) && aligned(k_hist) && aligned(v_hist) && aligned(k_intra) &&
+                      aligned(v_intra) && aligned(o_sparse) && aligned(n_sel, 4),
+                  HSAKV_ERR_MISALIGNED);
+    const Geo g = make_geo(dims);
+    HSAKV_CHECK(check_ws(ws, ws_bytes, ws_sparse(g)));
+    Epi ep{o_sparse, nullptr, nullptr, nullptr, nullptr, nullptr};
+    launch_sparse_compute_bf16(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, ws, ep, (hipStream_t)stream);
+    return done();
+}
+
 HSAKV_API int hsa_linear_branch(const hsakv_dims* dims, const void* q, const void* k_hist,
                                 const void* v_hist, const void* k_intra, const void* v_intra,
                                 const int32_t* n_sel, const void* E, const void* F,

@@ -54,7 +54,7 @@ EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
     "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
-    "hsa_sparse_attn_static", "hkv_page_commit",
+    "hsa_sparse_attn_static", "hkv_page_commit", "hsa_sparse_plan", "hsa_sparse_compute",
 ]
 
 
@@ -135,6 +135,8 @@ _sig = {
     "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Retrieval), ctypes.POINTER(Inputs),
                               ctypes.POINTER(Outputs), _P, c_size_t, _P, ctypes.POINTER(Fork)]),
     "hsa_sparse_attn_static": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hsa_sparse_plan": (c_int32, [_D, _P, _P, _P, _P, c_size_t, _P]),
+    "hsa_sparse_compute": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hkv_page_commit": (c_int32, [_D, _P, _P, _P, _P, _P, _P, c_int32, ctypes.c_int64, c_int32, _P, c_size_t,
                                   _P]),
     "hsakv_fork_create": (c_int32, [ctypes.POINTER(Fork)]),
@@ -270,6 +272,20 @@ def hsa_sparse_attn(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_
     _check("hsa_sparse_attn", _lib.hsa_sparse_attn(
         ctypes.byref(dims), _ptr(q), _ptr(k_hist), _ptr(v_hist), _ptr(k_intra), _ptr(v_intra),
         _ptr(n_sel), _ptr(sel_count), _ptr(sel_idx), _ptr(o_sparse), w, wb, _stream(stream)))
+
+
+def hsa_sparse_plan(dims: Dims, n_sel, sel_count, sel_idx, ws, stream=None) -> None:
+    w, wb = _ws(ws)
+    _check("hsa_sparse_plan", _lib.hsa_sparse_plan(
+        ctypes.byref(dims), _ptr(n_sel), _ptr(sel_count), _ptr(sel_idx), w, wb, _stream(stream)))
+
+
+def hsa_sparse_compute(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, o_sparse, ws,
+                       stream=None) -> None:
+    w, wb = _ws(ws)
+    _check("hsa_sparse_compute", _lib.hsa_sparse_compute(
+        ctypes.byref(dims), _ptr(q), _ptr(k_hist), _ptr(v_hist), _ptr(k_intra), _ptr(v_intra),
+        _ptr(n_sel), _ptr(o_sparse), w, wb, _stream(stream)))
 
 
 def hsa_sparse_attn_static(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,

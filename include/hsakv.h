@@ -301,6 +301,23 @@ int hsa_sparse_attn(const hsakv_dims* dims, const void* q, const void* k_hist, c
                     const int32_t* sel_count, const int32_t* sel_idx, float* o_sparse,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* hsa_sparse_attn (bf16) in its two parts, for callers that run the plan
+ * beside other work (as hsa_forward does) or time the attention alone.
+ * hsa_sparse_plan reads the selection only (n_sel, sel_count, sel_idx) and
+ * writes the work plan into the workspace: the rows of each head grouped
+ * four at a time by selection overlap, each group's union of selected
+ * blocks as 64-key tiles, and the global tile sequence. hsa_sparse_compute
+ * then runs the attention over that plan and merges split groups, writing
+ * o_sparse exactly as hsa_sparse_attn does. Both take the same workspace
+ * (HSAKV_ENTRY_SPARSE), which must not change between the two calls;
+ * compute must be ordered after plan. float32 data returns
+ * HSAKV_ERR_BAD_DTYPE (its attention has no separate plan). */
+int hsa_sparse_plan(const hsakv_dims* dims, const int32_t* n_sel, const int32_t* sel_count,
+                    const int32_t* sel_idx, void* ws, size_t ws_bytes, void* stream);
+int hsa_sparse_compute(const hsakv_dims* dims, const void* q, const void* k_hist, const void* v_hist,
+                       const void* k_intra, const void* v_intra, const int32_t* n_sel, float* o_sparse,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* hsa_sparse_attn without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. Arguments,

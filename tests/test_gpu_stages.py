@@ -16,7 +16,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 from block_sparse_rank_amd import hsakv as hs  # noqa: E402
 from gpu_util import (Case, check_selection, compare, dev, expected_sparse, host,  # noqa: E402
-                      pack_selection)
+                      pack_selection, ws)
 
 
 def _variant(name, **over):
@@ -215,6 +215,21 @@ def test_forward_with_only_out(case):
     full = host(case.forward(km)["out"])
     bare = host(case.forward(km, debug=False)["out"])
     assert full.tobytes() == bare.tobytes()
+
+
+def test_sparse_plan_then_compute_equals_entry_point(case):
+    """The attention in its two exported parts gives the bits of hsa_sparse_attn."""
+    s = case.s
+    if s.dtype != "bf16":
+        pytest.skip("the plan/compute split is the bf16 path")
+    _, n_sel, k_hist, v_hist = case.gather(case.page_summary())
+    cnt, idx, _, _ = case.select(k_hist, n_sel)
+    ref = case.sparse(k_hist, v_hist, n_sel, cnt, idx)
+    w = ws(case.d, hs.ENTRY_SPARSE)
+    o = torch.full((s.Lq, s.H, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    hs.hsa_sparse_plan(case.d, n_sel, cnt, idx, w)
+    hs.hsa_sparse_compute(case.d, case.t["q"], k_hist, v_hist, case.t["k_intra"], case.t["v_intra"], n_sel, o, w)
+    assert host(o).tobytes() == host(ref).tobytes()
 
 
 def test_forward_on_one_stream_equals_forked(case):

@@ -137,6 +137,20 @@ def test_page_commit_rejects_before_launch():
     assert hs._lib.hsakv_last_hip_error() == 0
 
 
+def test_sparse_plan_and_compute_reject_before_launch():
+    d = _dims()
+    need = hs.workspace_bytes(d, hs.ENTRY_SPARSE)
+    assert hs._lib.hsa_sparse_plan(ctypes.byref(_dims(dtype="f32")), FAKE, FAKE, FAKE, FAKE, need, None) == \
+        hs.ERR_BAD_DTYPE
+    assert hs._lib.hsa_sparse_plan(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need - 1, None) == hs.ERR_WORKSPACE
+    assert hs._lib.hsa_sparse_plan(ctypes.byref(d), None, FAKE, FAKE, FAKE, need, None) == hs.ERR_NULL_ARG
+    assert hs._lib.hsa_sparse_compute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
+                                      need, None) == hs.ERR_WORKSPACE
+    assert hs._lib.hsa_sparse_compute(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      need, None) == hs.ERR_NULL_ARG
+    assert hs._lib.hsakv_last_hip_error() == 0
+
+
 def test_null_dims():
     assert hs._lib.hsakv_validate(None) == hs.ERR_NULL_ARG
 
