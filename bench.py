@@ -49,7 +49,7 @@ def parse():
                     choices=["two_stage", "page_only", "prompt_only", "recent", "random", "mismatched"],
                     help="retrieval policy of the forward (the method's is two_stage)")
     ap.add_argument("--seed", type=int, default=0, help="seed of the random retrieval policy")
-    ap.add_argument("--sweep", default=None, choices=["psize-kp", "policies"],
+    ap.add_argument("--sweep", default=None, choices=["psize-kp", "policies", "tiers"],
                     help="instead of the benchmark line, one JSON line per configuration: "
                          "(Psize, Kp) at a fixed history length, or every retrieval policy on the "
                          "60 s workload")
@@ -241,6 +241,8 @@ def sweep(a):
     from block_sparse_rank_amd import hsakv as hs
 
     import synth
+    if a.sweep == "tiers":
+        return sweep_tiers(a)
     if a.sweep == "psize-kp":
         base = synth.shape("wan1.3b-480p")
         confs = [(dict(Psize=ps, P=256 // ps, Kp=kp), "two_stage") for ps in (4, 8, 16) for kp in (2, 4, 8)
@@ -298,6 +300,76 @@ def commit_time(a, s, T, hs, torch, stream):
     return {"ms": round(ms, 4), "tokens": n, "pages_completed": completes, "bound": "hbm",
             "algorithmic_bytes": nbytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def sweep_tiers(a):
+    """Tiered pages on the Wan-1.3B 480p chunk-layer: every page in the pinned
+    host store, 8 HBM slots. Times the forward with the retrieved pages all in
+    HBM slots (after the planner promoted them) and with none (read from the
+    host store over the bus), the promotion itself, and the HBM the pool takes
+    against the history it serves."""
+    import torch
+
+    import synth
+    from block_sparse_rank_amd import hsakv as hs
+    s = synth.shape("wan1.3b-480p")
+    run = time_forward(s, 2, 1)           # uploads the chunk-layer; its all-HBM times are the reference
+    d, T, stream = run["d"], run["T"], run["stream"]
+    slots = 8
+    hk = hs.HostStore(run["pool_k"].shape, run["pool_k"].dtype)
+    hv = hs.HostStore(run["pool_v"].shape, run["pool_v"].dtype)
+    hk.array[:] = run["pool_k"]
+    hv.array[:] = run["pool_v"]
+    pk = torch.zeros((slots, s.Tp, s.H, s.d), dtype=T["q"].dtype, device=T["q"].device)
+    pv = torch.zeros_like(pk)
+    table = torch.full((s.P,), -1, dtype=torch.int32, device=pk.device)
+    tiers = hs.Tiers(table.data_ptr(), hk.device, hv.device)
+    pl = hs.TierPlacement(s.P, slots)
+    outs = {"out": torch.empty((s.Lq, s.H, s.d), dtype=T["q"].dtype, device=pk.device),
+            "n_sel": run["n_sel"], "page_idx": torch.empty(s.Kp, dtype=torch.int32, device=pk.device)}
+    ins = {k: T[k] for k in ("q", "k_intra", "v_intra", "E", "F", "w_g", "b_g", "page_prompt")}
+    ins.update(pool_k=pk, pool_v=pv, page_kmean=run["page_kmean"])
+    ws = torch.empty(hs.workspace_bytes(d, hs.ENTRY_FORWARD), dtype=torch.uint8, device=pk.device)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(reps):
+            fn()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / reps
+
+    fwd = lambda: hs.hsa_forward(d, run["tau"], s.cur_prompt, ins, outs, ws, stream=stream,  # noqa: E731
+                                 fork=run["fork"], tiers=tiers)
+    miss_ms = timed(fwd, max(2, a.steps // 4))
+    torch.cuda.synchronize()
+    n = int(outs["n_sel"].cpu()[0])
+    pages = outs["page_idx"].cpu().tolist()[:n]
+    pp, ps, up, uv = hs.hkv_tier_plan(pl, 1, pages)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    hs.hkv_tier_apply(d, tiers, pk, pv, slots, pp, ps, up, uv, stream=stream)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    apply_ms = e[0].elapsed_time(e[1])
+    hit_ms = timed(fwd, a.steps)
+    page_bytes = 2 * s.Tp * s.H * s.d * 2
+    line = {"sweep": "tiers", "workload": s.name, "P": s.P, "hbm_slots": slots, "retrieved": pages,
+            "forward_all_hbm_pool_ms": round(run["warm_ms"], 4),
+            "forward_pages_in_hbm_slots_ms": round(hit_ms, 4),
+            "forward_pages_from_host_store_ms": round(miss_ms, 4),
+            "promote_pages_ms": round(apply_ms, 4), "promoted": len(pp),
+            "promote_GBps": round(len(pp) * page_bytes / (apply_ms * 1e-3) / 1e9, 1),
+            "hbm_pool_bytes": slots * page_bytes, "history_bytes": s.P * page_bytes}
+    hs.fork_destroy(run["fork"])
+    torch.cuda.synchronize()
+    hk.free()
+    hv.free()
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def forward_floor(s, n_sel, sparse_flops):

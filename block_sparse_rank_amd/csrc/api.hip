@@ -171,16 +171,34 @@ int check_policy(const hsakv_retrieval* r) {
     return HSAKV_OK;
 }
 
+Tiers tiers_of(const hsakv_tiers* t) {
+    Tiers r{nullptr, nullptr, nullptr};
+    if (t) {
+        r.page_slot = t->page_slot;
+        r.host_k = t->host_k;
+        r.host_v = t->host_v;
+    }
+    return r;
+}
+
+int check_tiers(const hsakv_tiers* t) {
+    if (!t) return HSAKV_OK;
+    if (!t->page_slot || !t->host_k || !t->host_v) return HSAKV_ERR_NULL_ARG;
+    if (!aligned(t->page_slot, 4) || !aligned(t->host_k) || !aligned(t->host_v)) return HSAKV_ERR_MISALIGNED;
+    return HSAKV_OK;
+}
+
 template <typename T>
 void run_gather(const Geo& g, const void* pool_k, const void* pool_v, const float* page_kmean,
-                const int32_t* page_prompt, int cur_prompt, const Policy& pol, const void* q, int32_t* page_idx,
-                int32_t* n_sel, void* k_hist, void* v_hist, float* partial, float* kb, hipStream_t st) {
+                const int32_t* page_prompt, int cur_prompt, const Policy& pol, const Tiers& tiers, const void* q,
+                int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist, float* partial, float* kb,
+                hipStream_t st) {
     launch_q_partials<T>(g, q, partial, st);
     launch_retrieve(g, partial, page_kmean, page_prompt, cur_prompt, pol.policy, pol.seed, page_idx, n_sel, st);
     if (kb)   // the history blocks of the pooled keys come with the copy
-        launch_gather_pool<T>(g, pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, kb, st);
+        launch_gather_pool<T>(g, pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, kb, tiers, st);
     else
-        launch_gather(g, (int)sizeof(T), pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, st);
+        launch_gather(g, (int)sizeof(T), pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, tiers, st);
 }
 
 template <typename T>
@@ -330,11 +348,12 @@ HSAKV_API int hkv_page_commit(const hsakv_dims* dims, void* pool_k, void* pool_v
 
 HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void* pool_v,
                          const float* page_kmean, const int32_t* page_prompt, int32_t cur_prompt,
-                         const hsakv_retrieval* retrieval, const void* q, int32_t* page_idx,
-                         int32_t* n_sel, void* k_hist, void* v_hist, void* ws, size_t ws_bytes,
-                         void* stream) {
+                         const hsakv_retrieval* retrieval, const hsakv_tiers* tiers, const void* q,
+                         int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist, void* ws,
+                         size_t ws_bytes, void* stream) {
     HSAKV_CHECK(check_dims(dims));
     HSAKV_CHECK(check_policy(retrieval));
+    HSAKV_CHECK(check_tiers(tiers));
     HSAKV_REQUIRE(pool_k && pool_v && page_kmean && page_prompt && q && page_idx && n_sel &&
                       k_hist && v_hist,
                   HSAKV_ERR_NULL_ARG);
@@ -346,10 +365,12 @@ HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void*
     HSAKV_CHECK(check_ws(ws, ws_bytes, ws_gather(g)));
     hipStream_t st = (hipStream_t)stream;
     if (dims->dtype == HSAKV_BF16)
-        run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval), q, page_idx,
+        run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval),
+                           tiers_of(tiers), q, page_idx,
                            n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     else
-        run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval), q, page_idx,
+        run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval),
+                          tiers_of(tiers), q, page_idx,
                           n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
     return done();
 }
@@ -517,11 +538,13 @@ HSAKV_API int hsakv_fork_destroy(hsakv_fork* f) {
 }
 
 HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
-                          const hsakv_retrieval* retrieval, const hsakv_inputs* in,
-                          hsakv_outputs* out, void* ws, size_t ws_bytes, void* stream,
-                          const hsakv_fork* fork) {
+                          const hsakv_retrieval* retrieval, const hsakv_tiers* tiers,
+                          const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
+                          void* stream, const hsakv_fork* fork) {
     HSAKV_CHECK(check_dims(dims));
     HSAKV_CHECK(check_policy(retrieval));
+    HSAKV_CHECK(check_tiers(tiers));
+    const Tiers tr = tiers_of(tiers);
     const Policy pol = policy_of(retrieval);
     HSAKV_REQUIRE(in && out, HSAKV_ERR_NULL_ARG);
     HSAKV_CHECK(check_tau(dims, tau));
@@ -569,7 +592,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     Epi ep{out->o_sparse, out->out, o_linear, out->gate, in->w_g, in->b_g};
     hipStream_t st = (hipStream_t)stream;
     if (eb == 2) {
-        run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol,
+        run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol, tr,
                            in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         // The low-rank branch needs the gathered KV only: with a fork it runs
         // on the caller's second stream beside the pooling, the block
@@ -606,7 +629,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
         launch_sparse_compute_bf16(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, sparse_ws, ep,
                                    st);
     } else {
-        run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol,
+        run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol, tr,
                           in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                           nullptr, qb, kb, zl, true, st);
@@ -681,5 +704,120 @@ HSAKV_API int hsa_sparse_attn_static(const hsakv_dims* dims, const void* q, cons
     else
         launch_sparse_attn<float>(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, sel_count,
                                   sel_idx, ws, ep, st);
+    return done();
+}
+
+// ---- page tiers: HBM slots caching pages of a pinned host store ----------------
+
+HSAKV_API int hsakv_host_alloc(size_t bytes, void** host_ptr, void** device_ptr) {
+    if (!host_ptr || !device_ptr) return HSAKV_ERR_NULL_ARG;
+    *host_ptr = *device_ptr = nullptr;
+    void* h = nullptr;
+    hipError_t e = hipHostMalloc(&h, bytes ? bytes : 1, hipHostMallocMapped);
+    void* d = nullptr;
+    if (e == hipSuccess) e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess) {
+        if (h) (void)hipHostFree(h);
+        g_last_hip_error = (int)e;
+        return HSAKV_ERR_HIP;
+    }
+    *host_ptr = h;
+    *device_ptr = d;
+    return HSAKV_OK;
+}
+
+HSAKV_API int hsakv_host_free(void* host_ptr) {
+    if (!host_ptr) return HSAKV_OK;
+    const hipError_t e = hipHostFree(host_ptr);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return HSAKV_ERR_HIP;
+    }
+    return HSAKV_OK;
+}
+
+HSAKV_API int hkv_tier_plan(int32_t P, int32_t slots, int32_t* slot_of_page, int32_t* page_of_slot,
+                            int64_t* last_use, int64_t now, const int32_t* want, int32_t n_want,
+                            int32_t* promote_page, int32_t* promote_slot, int32_t* n_promote,
+                            int32_t* upd_page, int32_t* upd_value, int32_t* n_upd) {
+    if (!slot_of_page || !page_of_slot || !last_use || (n_want > 0 && !want) || !promote_page ||
+        !promote_slot || !n_promote || !upd_page || !upd_value || !n_upd)
+        return HSAKV_ERR_NULL_ARG;
+    if (P < 1 || slots < 0 || n_want < 0) return HSAKV_ERR_BAD_DIMS;
+    for (int i = 0; i < n_want; ++i)
+        if (want[i] < 0 || want[i] >= P) return HSAKV_ERR_BAD_DIMS;
+    // the wanted pages are the most recently used from now on
+    for (int i = 0; i < n_want; ++i) last_use[want[i]] = now;
+    int np = 0, nu = 0;
+    for (int i = 0; i < n_want; ++i) {
+        const int p = want[i];
+        if (slot_of_page[p] >= 0) continue;
+        // a free slot, else the slot of the least recently used page not wanted now
+        int best = -1;
+        long long best_use = 0;
+        for (int s = 0; s < slots; ++s) {
+            const int q = page_of_slot[s];
+            if (q < 0) {
+                best = s;
+                break;
+            }
+            if (last_use[q] >= now) continue;
+            if (best < 0 || last_use[q] < best_use) {
+                best = s;
+                best_use = last_use[q];
+            }
+        }
+        if (best < 0) break;   // every slot holds a page wanted now
+        const int victim = page_of_slot[best];
+        if (victim >= 0) {
+            slot_of_page[victim] = -1;
+            upd_page[nu] = victim;
+            upd_value[nu++] = -1;
+        }
+        slot_of_page[p] = best;
+        page_of_slot[best] = p;
+        upd_page[nu] = p;
+        upd_value[nu++] = best;
+        promote_page[np] = p;
+        promote_slot[np++] = best;
+    }
+    *n_promote = np;
+    *n_upd = nu;
+    return HSAKV_OK;
+}
+
+HSAKV_API int hkv_tier_apply(const hsakv_dims* dims, const hsakv_tiers* tiers, void* pool_k, void* pool_v,
+                             int32_t slots, const int32_t* promote_page, const int32_t* promote_slot,
+                             int32_t n_promote, const int32_t* upd_page, const int32_t* upd_value,
+                             int32_t n_upd, void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(tiers && pool_k && pool_v, HSAKV_ERR_NULL_ARG);
+    HSAKV_CHECK(check_tiers(tiers));
+    HSAKV_REQUIRE(aligned(pool_k) && aligned(pool_v), HSAKV_ERR_MISALIGNED);
+    HSAKV_REQUIRE(n_promote >= 0 && n_upd >= 0 && n_upd <= 256 && slots >= 0, HSAKV_ERR_BAD_DIMS);
+    HSAKV_REQUIRE((n_promote == 0 || (promote_page && promote_slot)) && (n_upd == 0 || (upd_page && upd_value)),
+                  HSAKV_ERR_NULL_ARG);
+    const Geo g = make_geo(dims);
+    for (int i = 0; i < n_promote; ++i)
+        if (promote_page[i] < 0 || promote_page[i] >= g.P || promote_slot[i] < 0 || promote_slot[i] >= slots)
+            return HSAKV_ERR_BAD_DIMS;
+    for (int i = 0; i < n_upd; ++i)
+        if (upd_page[i] < 0 || upd_page[i] >= g.P || upd_value[i] < -1 || upd_value[i] >= slots)
+            return HSAKV_ERR_BAD_DIMS;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t page_bytes = (size_t)g.Tp * g.HD * g.elt;
+    for (int i = 0; i < n_promote; ++i) {
+        const size_t src = (size_t)promote_page[i] * page_bytes, dst = (size_t)promote_slot[i] * page_bytes;
+        hipError_t e = hipMemcpyAsync((char*)pool_k + dst, (const char*)tiers->host_k + src, page_bytes,
+                                      hipMemcpyDefault, st);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync((char*)pool_v + dst, (const char*)tiers->host_v + src, page_bytes, hipMemcpyDefault,
+                               st);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return HSAKV_ERR_HIP;
+        }
+    }
+    if (n_upd > 0) launch_tier_table(tiers->page_slot, n_upd, upd_page, upd_value, st);
     return done();
 }

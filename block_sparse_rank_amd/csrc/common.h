@@ -25,6 +25,17 @@ struct Geo {
     int elt;              // bytes per element of the storage type (2 bf16, 4 f32)
 };
 
+// Where a page's rows are read from. Without a page table (page_slot null)
+// page p is page p of the HBM pool. With one, page_slot[p] >= 0 is the HBM
+// pool slot caching the page, and page_slot[p] < 0 means the page is only in
+// the pinned host store (host_k / host_v, indexed by page id), which the
+// kernels read directly over the bus.
+struct Tiers {
+    const int32_t* page_slot;
+    const void* host_k;
+    const void* host_v;
+};
+
 // Per-head thresholds passed by value in the kernel arguments, so no host to
 // device copy is needed (and the call stays capturable).
 constexpr int kMaxHeads = 256;

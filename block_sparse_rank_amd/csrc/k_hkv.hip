@@ -199,14 +199,24 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 8;
 
+// First element of page `page` (K or V) in its tier: HBM pool slot or host store.
+template <typename E>
+HSAKV_DEV const E* page_base(const E* pool, const Tiers& t, bool is_k, long long page, long long per_page) {
+    if (!t.page_slot) return pool + page * per_page;
+    const int slot = t.page_slot[page];
+    if (slot >= 0) return pool + (long long)slot * per_page;
+    return (const E*)(is_k ? t.host_k : t.host_v) + page * per_page;
+}
+
 __global__ void __launch_bounds__(kGatherThreads)
 k_gather(const u32x4* __restrict__ pool_k, const u32x4* __restrict__ pool_v,
          const int32_t* __restrict__ page_idx, const int32_t* __restrict__ n_sel,
-         u32x4* __restrict__ k_hist, u32x4* __restrict__ v_hist, long long vec_per_page) {
+         u32x4* __restrict__ k_hist, u32x4* __restrict__ v_hist, long long vec_per_page, Tiers tiers) {
     const int slot = blockIdx.y;
     if (slot >= *n_sel) return;
     const long long page = page_idx[slot];
-    const u32x4* src = (blockIdx.z == 0 ? pool_k : pool_v) + page * vec_per_page;
+    const bool is_k = blockIdx.z == 0;
+    const u32x4* src = page_base(is_k ? pool_k : pool_v, tiers, is_k, page, vec_per_page);
     u32x4* dst = (blockIdx.z == 0 ? k_hist : v_hist) + (long long)slot * vec_per_page;
     const long long chunk = (long long)kGatherThreads * kGatherUnroll;
     for (long long base = (long long)blockIdx.x * chunk; base < vec_per_page;
@@ -271,7 +281,7 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
               const int32_t* __restrict__ page_idx, const int32_t* __restrict__ n_sel_p,
-              T* __restrict__ k_hist, T* __restrict__ v_hist, float* __restrict__ kb) {
+              T* __restrict__ k_hist, T* __restrict__ v_hist, float* __restrict__ kb, Tiers tiers) {
     constexpr int kRows = sizeof(T) == 2 ? 16 : 8;   // rows in flight per thread
     const int n_sel = *n_sel_p;
     const int nslab = (g.HD + 255) / 256;
@@ -287,14 +297,14 @@ k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
     T* dst = is_k ? k_hist : v_hist;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // rows t, t + 8, ... of this thread's group, kRows loads in flight; row
-    // tu of the active history is row srow(tu) of the pool
+    // tu of the active history starts at srow(tu)
     auto copy_rows = [&](auto srow) __attribute__((always_inline)) {
         for (long long t = t0 + grp; t < t1; t += 8 * kRows) {
             Row8<T> v[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
                 const long long tu = t + 8 * u;
-                if (tu < t1) v[u].load(src + srow(tu) * g.HD + col0);
+                if (tu < t1) v[u].load(srow(tu) + col0);
             }
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
@@ -309,20 +319,24 @@ k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
     if (col0 < g.HD) {
         const int slot0 = (int)(t0 / g.Tp);
         const long long first0 = (long long)slot0 * g.Tp;
+        const long long per_page = (long long)g.Tp * g.HD;
         if (g.Binter <= g.Tp) {
             // the block touches the pages of slot0 and slot0 + 1 at most: both
             // looked up once, so no row load waits for a page lookup
             const long long pa = page_idx[slot0];
             const long long pb = slot0 + 1 < n_sel ? page_idx[slot0 + 1] : pa;
+            const T* ba = page_base(src, tiers, is_k, pa, per_page);
+            const T* bb = page_base(src, tiers, is_k, pb, per_page);
             copy_rows([&](long long tu) {
                 const long long rel = tu - first0;
-                return rel < g.Tp ? pa * g.Tp + rel : pb * g.Tp + (rel - g.Tp);
+                return rel < g.Tp ? ba + rel * g.HD : bb + (rel - g.Tp) * g.HD;
             });
         } else {
             // short pages: several per block, each row looks its page up
             copy_rows([&](long long tu) {
                 const long long slot = tu / g.Tp;
-                return (long long)page_idx[slot] * g.Tp + (tu - slot * g.Tp);
+                return page_base(src, tiers, is_k, (long long)page_idx[slot], per_page) +
+                       (tu - slot * g.Tp) * g.HD;
             });
         }
     }
@@ -343,26 +357,27 @@ k_gather_pool(Geo g, const T* __restrict__ pool_k, const T* __restrict__ pool_v,
 
 template <typename T>
 void launch_gather_pool(const Geo& g, const void* pool_k, const void* pool_v, const int32_t* page_idx,
-                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, hipStream_t st) {
+                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, const Tiers& tiers,
+                        hipStream_t st) {
     dim3 grid((unsigned)((long long)g.NBh_max * ((g.HD + 255) / 256)), 2);
     hipLaunchKernelGGL(k_gather_pool<T>, grid, dim3(256), 0, st, g, (const T*)pool_k, (const T*)pool_v,
-                       page_idx, n_sel, (T*)k_hist, (T*)v_hist, kb);
+                       page_idx, n_sel, (T*)k_hist, (T*)v_hist, kb, tiers);
 }
 template void launch_gather_pool<float>(const Geo&, const void*, const void*, const int32_t*, const int32_t*,
-                                        void*, void*, float*, hipStream_t);
+                                        void*, void*, float*, const Tiers&, hipStream_t);
 template void launch_gather_pool<bf16_t>(const Geo&, const void*, const void*, const int32_t*, const int32_t*,
-                                         void*, void*, float*, hipStream_t);
+                                         void*, void*, float*, const Tiers&, hipStream_t);
 
 void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* pool_v,
                    const int32_t* page_idx, const int32_t* n_sel, void* k_hist, void* v_hist,
-                   hipStream_t st) {
+                   const Tiers& tiers, hipStream_t st) {
     long long vec = (long long)g.Tp * g.HD * elt_bytes / 16;
     long long chunk = (long long)kGatherThreads * kGatherUnroll;
     long long blocks = (vec + chunk - 1) / chunk;
     if (blocks > 4096) blocks = 4096;
     dim3 grid((unsigned)blocks, g.Kp, 2);
     hipLaunchKernelGGL(k_gather, grid, dim3(kGatherThreads), 0, st, (const u32x4*)pool_k,
-                       (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec);
+                       (const u32x4*)pool_v, page_idx, n_sel, (u32x4*)k_hist, (u32x4*)v_hist, vec, tiers);
 }
 
 // Page means in two deterministic passes, so a page's mean does not depend on
@@ -524,3 +539,29 @@ template void launch_page_commit<float>(const Geo&, void*, void*, float*, int32_
                                         long long, int, float*, hipStream_t);
 template void launch_page_commit<bf16_t>(const Geo&, void*, void*, float*, int32_t*, const void*, const void*, int,
                                          long long, int, float*, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Tier moves: page_slot[page] = value for each (page, value) update, after
+// the promotions' page copies that precede it on the stream.
+
+constexpr int kMaxTierUpdates = 256;
+struct TierUpdates {
+    int n;
+    int page[kMaxTierUpdates];
+    int value[kMaxTierUpdates];
+};
+
+__global__ void k_tier_table(int32_t* __restrict__ page_slot, TierUpdates u) {
+    const int i = threadIdx.x;
+    if (i < u.n) page_slot[u.page[i]] = u.value[i];
+}
+
+void launch_tier_table(int32_t* page_slot, int n, const int32_t* pages, const int32_t* values, hipStream_t st) {
+    TierUpdates u;
+    u.n = n;
+    for (int i = 0; i < n; ++i) {
+        u.page[i] = pages[i];
+        u.value[i] = values[i];
+    }
+    hipLaunchKernelGGL(k_tier_table, dim3(1), dim3(kMaxTierUpdates), 0, st, page_slot, u);
+}

@@ -39,11 +39,14 @@ void launch_retrieve(const Geo&, const float* partial, const float* page_kmean, 
                      int cur_prompt, int policy, unsigned long long seed, int32_t* page_idx, int32_t* n_sel,
                      hipStream_t);
 void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* pool_v, const int32_t* page_idx,
-                   const int32_t* n_sel, void* k_hist, void* v_hist, hipStream_t);
+                   const int32_t* n_sel, void* k_hist, void* v_hist, const Tiers& tiers, hipStream_t);
 // The gather with the history blocks of the pooled keys kb written on the way.
 template <typename T>
 void launch_gather_pool(const Geo&, const void* pool_k, const void* pool_v, const int32_t* page_idx,
-                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, hipStream_t);
+                        const int32_t* n_sel, void* k_hist, void* v_hist, float* kb, const Tiers& tiers,
+                        hipStream_t);
+// Page-table updates page_slot[pages[i]] = values[i], i < n <= 256.
+void launch_tier_table(int32_t* page_slot, int n, const int32_t* pages, const int32_t* values, hipStream_t);
 
 // hist_pooled: the history blocks of kb are already written (launch_gather_pool)
 template <typename T>

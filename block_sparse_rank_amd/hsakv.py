@@ -55,6 +55,7 @@ EXPORTS = [
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
     "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
     "hsa_sparse_attn_static", "hkv_page_commit", "hsa_sparse_plan", "hsa_sparse_compute",
+    "hsakv_host_alloc", "hsakv_host_free", "hkv_tier_plan", "hkv_tier_apply",
 ]
 
 
@@ -111,6 +112,19 @@ def _retrieval(policy, seed):
     return ctypes.byref(Retrieval(pid, 0, int(seed)))
 
 
+class Tiers(ctypes.Structure):
+    """hsakv_tiers: device page table and the device addresses of the pinned host store."""
+    _fields_ = [("page_slot", c_void_p), ("host_k", c_void_p), ("host_v", c_void_p)]
+
+
+def make_tiers(page_slot, host_k, host_v) -> Tiers:
+    return Tiers(_ptr(page_slot), _ptr(host_k), _ptr(host_v))
+
+
+def _tiers(t):
+    return ctypes.byref(t) if t is not None else None
+
+
 class Fork(ctypes.Structure):
     """hsakv_fork: a caller-owned second stream and two events (hipStream_t,
     hipEvent_t handles) for hsa_forward's low-rank branch."""
@@ -126,14 +140,21 @@ _sig = {
     "hsakv_validate": (c_int32, [_D]),
     "hsakv_workspace_bytes": (c_size_t, [_D, c_int32]),
     "hkv_page_summary": (c_int32, [_D, _P, _P, _P, c_size_t, _P]),
-    "hkv_gather": (c_int32, [_D, _P, _P, _P, _P, c_int32, ctypes.POINTER(Retrieval), _P, _P, _P, _P, _P, _P,
-                             c_size_t, _P]),
+    "hkv_gather": (c_int32, [_D, _P, _P, _P, _P, c_int32, ctypes.POINTER(Retrieval), ctypes.POINTER(Tiers), _P,
+                             _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_select": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_sparse_attn": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_linear_branch": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_fuse": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P]),
-    "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Retrieval), ctypes.POINTER(Inputs),
-                              ctypes.POINTER(Outputs), _P, c_size_t, _P, ctypes.POINTER(Fork)]),
+    "hsa_forward": (c_int32, [_D, _P, c_int32, ctypes.POINTER(Retrieval), ctypes.POINTER(Tiers),
+                              ctypes.POINTER(Inputs), ctypes.POINTER(Outputs), _P, c_size_t, _P,
+                              ctypes.POINTER(Fork)]),
+    "hsakv_host_alloc": (c_int32, [c_size_t, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p)]),
+    "hsakv_host_free": (c_int32, [_P]),
+    "hkv_tier_plan": (c_int32, [c_int32, c_int32, _P, _P, _P, ctypes.c_int64, _P, c_int32, _P, _P, _P, _P, _P,
+                                _P]),
+    "hkv_tier_apply": (c_int32, [_D, ctypes.POINTER(Tiers), _P, _P, c_int32, _P, _P, c_int32, _P, _P, c_int32,
+                                 _P]),
     "hsa_sparse_attn_static": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hsa_sparse_plan": (c_int32, [_D, _P, _P, _P, _P, c_size_t, _P]),
     "hsa_sparse_compute": (c_int32, [_D, _P, _P, _P, _P, _P, _P, _P, _P, c_size_t, _P]),
@@ -249,12 +270,13 @@ def hkv_page_commit(dims: Dims, pool_k, pool_v, page_kmean, page_prompt, k_chunk
 
 
 def hkv_gather(dims: Dims, pool_k, pool_v, page_kmean, page_prompt, cur_prompt: int, q, page_idx,
-               n_sel, k_hist, v_hist, ws, stream=None, policy=None, seed: int = 0) -> None:
+               n_sel, k_hist, v_hist, ws, stream=None, policy=None, seed: int = 0,
+               tiers: Optional[Tiers] = None) -> None:
     w, wb = _ws(ws)
     _check("hkv_gather", _lib.hkv_gather(
         ctypes.byref(dims), _ptr(pool_k), _ptr(pool_v), _ptr(page_kmean), _ptr(page_prompt),
-        int(cur_prompt), _retrieval(policy, seed), _ptr(q), _ptr(page_idx), _ptr(n_sel), _ptr(k_hist),
-        _ptr(v_hist), w, wb, _stream(stream)))
+        int(cur_prompt), _retrieval(policy, seed), _tiers(tiers), _ptr(q), _ptr(page_idx), _ptr(n_sel),
+        _ptr(k_hist), _ptr(v_hist), w, wb, _stream(stream)))
 
 
 def hsa_select(dims: Dims, q, k_hist, k_intra, n_sel, tau, sel_count, sel_idx, sel_mask=None,
@@ -324,11 +346,70 @@ def fork_destroy(f: Fork) -> None:
 
 
 def hsa_forward(dims: Dims, tau, cur_prompt: int, inputs: dict, outputs: dict, ws,
-                stream=None, fork: Optional[Fork] = None, policy=None, seed: int = 0) -> None:
+                stream=None, fork: Optional[Fork] = None, policy=None, seed: int = 0,
+                tiers: Optional[Tiers] = None) -> None:
     ins = Inputs(*[_ptr(inputs.get(n)) for n, _ in Inputs._fields_])
     outs = Outputs(*[_ptr(outputs.get(n)) for n, _ in Outputs._fields_])
     w, wb = _ws(ws)
     _check("hsa_forward", _lib.hsa_forward(
         ctypes.byref(dims), ctypes.cast(_host_f32(tau), c_void_p), int(cur_prompt),
-        _retrieval(policy, seed), ctypes.byref(ins), ctypes.byref(outs), w, wb, _stream(stream),
-        ctypes.byref(fork) if fork is not None else None))
+        _retrieval(policy, seed), _tiers(tiers), ctypes.byref(ins), ctypes.byref(outs), w, wb,
+        _stream(stream), ctypes.byref(fork) if fork is not None else None))
+
+
+# ---- page tiers ---------------------------------------------------------------
+
+class HostStore:
+    """Pinned, device-mapped host memory from hsakv_host_alloc: `array` is a
+    numpy view for the host, `device` the address kernels read."""
+
+    def __init__(self, shape, dtype):
+        import numpy as np
+        n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+        h, d = c_void_p(), c_void_p()
+        _check("hsakv_host_alloc", _lib.hsakv_host_alloc(n, ctypes.byref(h), ctypes.byref(d)))
+        self.host, self.device = h.value, d.value
+        buf = (ctypes.c_char * n).from_address(self.host)
+        self.array = np.frombuffer(buf, dtype=dtype).reshape(shape)
+
+    def free(self):
+        if self.host:
+            self.array = None
+            _check("hsakv_host_free", _lib.hsakv_host_free(self.host))
+            self.host = self.device = None
+
+
+class TierPlacement:
+    """Host copy of the HBM slot placement for hkv_tier_plan (int32/int64 numpy arrays)."""
+
+    def __init__(self, P: int, slots: int):
+        import numpy as np
+        self.P, self.slots = P, slots
+        self.slot_of_page = np.full(P, -1, np.int32)
+        self.page_of_slot = np.full(slots, -1, np.int32)
+        self.last_use = np.zeros(P, np.int64)
+
+
+def hkv_tier_plan(pl: TierPlacement, now: int, want):
+    """Returns (promote_page, promote_slot, upd_page, upd_value) numpy arrays."""
+    import numpy as np
+    want = np.ascontiguousarray(np.asarray(want, np.int32))
+    cap = max(1, min(len(want), pl.slots))
+    pp, ps = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+    up, uv = np.zeros(2 * cap, np.int32), np.zeros(2 * cap, np.int32)
+    npro, nupd = ctypes.c_int32(), ctypes.c_int32()
+    P = lambda a: a.ctypes.data_as(c_void_p)  # noqa: E731
+    _check("hkv_tier_plan", _lib.hkv_tier_plan(
+        pl.P, pl.slots, P(pl.slot_of_page), P(pl.page_of_slot), P(pl.last_use), int(now), P(want),
+        len(want), P(pp), P(ps), ctypes.byref(npro), P(up), P(uv), ctypes.byref(nupd)))
+    return pp[:npro.value].copy(), ps[:npro.value].copy(), up[:nupd.value].copy(), uv[:nupd.value].copy()
+
+
+def hkv_tier_apply(dims: Dims, tiers: Tiers, pool_k, pool_v, slots: int, promote_page, promote_slot,
+                   upd_page, upd_value, stream=None) -> None:
+    import numpy as np
+    a = [np.ascontiguousarray(np.asarray(x, np.int32)) for x in (promote_page, promote_slot, upd_page, upd_value)]
+    P = lambda x: x.ctypes.data_as(c_void_p) if len(x) else None  # noqa: E731
+    _check("hkv_tier_apply", _lib.hkv_tier_apply(
+        ctypes.byref(dims), ctypes.byref(tiers), _ptr(pool_k), _ptr(pool_v), int(slots), P(a[0]), P(a[1]),
+        len(a[0]), P(a[2]), P(a[3]), len(a[2]), _stream(stream)))

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HSAKV_VERSION 3
+#define HSAKV_VERSION 4
 
 /* status codes */
 #define HSAKV_OK                   0
@@ -145,6 +145,23 @@ typedef struct hsakv_retrieval {
     int32_t  reserved;   /* set to 0 */
     uint64_t seed;       /* RANDOM only */
 } hsakv_retrieval;
+
+/* Page tiers (HKV paragraph: pages live in tiers, GPU HBM above CPU DRAM,
+ * and unselected pages are demoted to the cheaper tier so that GPU memory
+ * does not grow with the video's length). The pinned host store holds every
+ * page, indexed by page id, as [P][Tp][H][d] (host_k, host_v: the device
+ * addresses of pinned host memory, e.g. from hsakv_host_alloc); the HBM
+ * pool (pool_k, pool_v of the calls below) then holds `slots` pages that
+ * cache some of them. page_slot (device int32 [P]) gives, for page p, its
+ * HBM slot (>= 0) or -1 when the page is only in the host store; the gather
+ * then reads it from host memory over the bus (slower, same bits). NULL
+ * tiers: page p is page p of the HBM pool (the whole pool in HBM).
+ * hkv_tier_apply writes page_slot; the gathers read it. */
+typedef struct hsakv_tiers {
+    int32_t*    page_slot;
+    const void* host_k;
+    const void* host_v;
+} hsakv_tiers;
 
 /* Inputs of the fused forward; every pointer is device memory. */
 typedef struct hsakv_inputs {
@@ -260,12 +277,13 @@ int hkv_page_commit(const hsakv_dims* dims, void* pool_k, void* pool_v, float* p
  *     for v; a bit copy. Rows at or past n_sel*Tp are not written.
  * q is [Lq][H][d] (device). cur_prompt is a host value. `retrieval` (host,
  * nullable) selects another policy for steps 1-2 (see hsakv_retrieval).
- * Workspace: HSAKV_ENTRY_GATHER. */
+ * `tiers` (host, nullable) reads the pages through a page table (see
+ * hsakv_tiers). Workspace: HSAKV_ENTRY_GATHER. */
 int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void* pool_v,
                const float* page_kmean, const int32_t* page_prompt, int32_t cur_prompt,
-               const hsakv_retrieval* retrieval, const void* q, int32_t* page_idx,
-               int32_t* n_sel, void* k_hist, void* v_hist, void* ws, size_t ws_bytes,
-               void* stream);
+               const hsakv_retrieval* retrieval, const hsakv_tiers* tiers, const void* q,
+               int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist, void* ws,
+               size_t ws_bytes, void* stream);
 
 /* Head-adaptive block selection (HSA paragraph: per head, the fewest blocks
  * whose cumulative attention mass reaches tau_h; Binter history blocks,
@@ -358,17 +376,53 @@ int hsa_fuse(const hsakv_dims* dims, const void* q, const float* w_g, const floa
 /* The whole chunk-layer: retrieval and gather, selection, linear branch,
  * sparse attention and the gate, with the gate fused into the sparse
  * attention's epilogue. Results equal the separate entry points run in that
- * order. tau (host, H floats), cur_prompt (host) and retrieval (host,
- * nullable) as above. Workspace: HSAKV_ENTRY_FORWARD.
+ * order. tau (host, H floats), cur_prompt (host), retrieval and tiers
+ * (host, nullable) as above. Workspace: HSAKV_ENTRY_FORWARD.
  * `fork` (host, nullable): with a fork whose stream is set and bf16 data, the
  * low-rank branch runs on the fork's stream beside the selection (see
  * hsakv_fork); NULL, or a fork with a NULL stream, runs everything on
  * `stream`. The results are the same either way. float32 data always runs on
  * `stream`. */
 int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
-                const hsakv_retrieval* retrieval, const hsakv_inputs* in,
-                hsakv_outputs* out, void* ws, size_t ws_bytes, void* stream,
-                const hsakv_fork* fork);
+                const hsakv_retrieval* retrieval, const hsakv_tiers* tiers,
+                const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
+                void* stream, const hsakv_fork* fork);
+
+/* ---- page tiers ---- */
+
+/* Pinned, device-mapped host memory for the host store (a set-up call, like
+ * hsakv_fork_create): *host_ptr for the host's own reads and writes,
+ * *device_ptr for hsakv_tiers. Freed with hsakv_host_free(host_ptr). */
+int hsakv_host_alloc(size_t bytes, void** host_ptr, void** device_ptr);
+int hsakv_host_free(void* host_ptr);
+
+/* Host-only least-recently-used planner of the HBM slots; touches no GPU.
+ * slot_of_page [P] (slot or -1), page_of_slot [slots] (page or -1) and
+ * last_use [P] are the caller's host copy of the placement, updated in
+ * place. The n_want pages of `want` (e.g. the pages the last forwards
+ * retrieved, then the newest pages) get last_use = now; each one not in a
+ * slot takes a free slot, else the slot of the least recently used page
+ * not wanted now (ties to the lower slot), which is demoted to the host
+ * store (its slot is simply reused: the host store keeps every page).
+ * Outputs: the promotions (promote_page[i] into promote_slot[i]; at most
+ * min(n_want, slots)) and the page-table updates (upd_page[i] gets
+ * upd_value[i]; at most 2 per promotion) for hkv_tier_apply. */
+int hkv_tier_plan(int32_t P, int32_t slots, int32_t* slot_of_page, int32_t* page_of_slot,
+                  int64_t* last_use, int64_t now, const int32_t* want, int32_t n_want,
+                  int32_t* promote_page, int32_t* promote_slot, int32_t* n_promote,
+                  int32_t* upd_page, int32_t* upd_value, int32_t* n_upd);
+
+/* Enqueues the promotions (host store page -> HBM slot copies of K and V,
+ * one page of Tp*H*d elements each) and then the page-table updates
+ * (n_upd <= 256) on `stream`. The arrays are host memory read before the
+ * call returns. Ordering: a slot must not be overwritten while a gather
+ * that reads its old page is still pending, and the next gather must see
+ * the new table: enqueue this after the previous forward's gather (e.g. on
+ * its fork stream) and make the next forward's stream wait for it. */
+int hkv_tier_apply(const hsakv_dims* dims, const hsakv_tiers* tiers, void* pool_k, void* pool_v,
+                   int32_t slots, const int32_t* promote_page, const int32_t* promote_slot,
+                   int32_t n_promote, const int32_t* upd_page, const int32_t* upd_value,
+                   int32_t n_upd, void* stream);
 
 #ifdef __cplusplus
 }

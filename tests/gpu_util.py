@@ -241,7 +241,7 @@ class Case:
         hs.hsa_fuse(d, self.t["q"], self.t["w_g"], self.t["b_g"], o_s, o_l, out, gate)
         return out, gate
 
-    def forward(self, page_kmean, debug=True, fork="default", policy=None, seed=0):
+    def forward(self, page_kmean, debug=True, fork="default", policy=None, seed=0, tiers=None):
         s, d = self.s, self.d
         outs = {"out": torch.zeros((s.Lq, s.H, s.d), dtype=tdtype(s), device="cuda")}
         if debug:
@@ -262,5 +262,5 @@ class Case:
         if fork == "default":
             fork = default_fork()
         hs.hsa_forward(d, self.ch["tau"], self.cur_prompt, ins, outs, ws(d, hs.ENTRY_FORWARD),
-                       fork=fork, policy=policy, seed=seed)
+                       fork=fork, policy=policy, seed=seed, tiers=tiers)
         return outs

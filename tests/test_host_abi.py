@@ -38,7 +38,7 @@ def test_header_declares_exactly_the_exports():
 
 
 def test_version_and_status_strings():
-    assert hs.version() == 3
+    assert hs.version() == 4
     for code in range(-9, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
@@ -180,14 +180,14 @@ def test_entry_points_reject_before_launch():
         _expect(hs.ERR_BAD_TAU, hs.hsa_select, d, FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE,
                 stream=0)
     # workspace missing, too small, misaligned
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, None, 0, None)
     assert st == hs.ERR_WORKSPACE
     need = hs.workspace_bytes(d, hs.ENTRY_GATHER)
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE, need - 1, None)
     assert st == hs.ERR_WORKSPACE
-    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, FAKE, FAKE,
+    st = hs._lib.hkv_gather(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0, None, None, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE + 16, need, None)
     assert st == hs.ERR_WORKSPACE
     # forward: null struct members
@@ -203,7 +203,7 @@ def test_entry_points_reject_before_launch():
     need = hs.workspace_bytes(d, hs.ENTRY_FORWARD)
     for ws_ptr, nbytes in ((FAKE, need - 1), (FAKE + 16, need), (None, need)):
         st = hs._lib.hsa_forward(ctypes.byref(d), ctypes.cast(hs._host_f32([0.5] * H), ctypes.c_void_p),
-                                 0, None, ctypes.byref(hs.Inputs(*[FAKE] * len(hs.Inputs._fields_))),
+                                 0, None, None, ctypes.byref(hs.Inputs(*[FAKE] * len(hs.Inputs._fields_))),
                                  ctypes.byref(hs.Outputs(FAKE)), ws_ptr, nbytes, None, None)
         assert st == hs.ERR_WORKSPACE
     # an unknown retrieval policy
