@@ -67,6 +67,7 @@ __all__ = [
     "page_commit",
     "POLICIES",
     "splitmix64_at",
+    "backward_params",
 ]
 
 
@@ -496,3 +497,57 @@ def page_commit(pool_k: np.ndarray, pool_v: np.ndarray, page_kmean: np.ndarray,
         km[p] = page_summary(as_f64(pk[p], dtype)[None])[0]
         pp[p] = cur_prompt
     return pk, pv, km, pp, done
+
+
+# ---------------------------------------------------------------------------
+# backward of the learned parameters (news summary, HSA paragraph: the gates
+# are learned; the Linformer projections E and F are the low-rank branch's
+# parameters)
+
+def backward_params(q: np.ndarray, K: np.ndarray, V: np.ndarray, E_act: np.ndarray, F_act: np.ndarray,
+                    w_g: np.ndarray, b_g: np.ndarray, o_s: np.ndarray, d_out: np.ndarray) -> Dict[str, np.ndarray]:
+    """Gradients of a loss with upstream gradient d_out = dLoss/dO with
+    respect to the gate parameters w_g [H][d], b_g [H] and the projections
+    E_act, F_act [r][L_act] (reading R28: the sparse branch has no learned
+    parameter and is held fixed).
+
+    With O = g O_s + (1 - g) O_l and g = sigma(x), x = <q, w_g[h]> + b_g[h]:
+      dLoss/dx = <d_out, O_s - O_l> g (1 - g),
+      dw_g[h] = sum_t dx[t, h] q[t, h],  db_g[h] = sum_t dx[t, h];
+    and for the low-rank branch, with dO_l = (1 - g) d_out, P = softmax(S),
+    S = q K'^T / sqrt(d), K' = E_act K_h, V' = F_act V_h (per head):
+      dV' = P^T dO_l,  dS = P * (dO_l V'^T - rowsum(dO_l * O_l)),
+      dK' = dS^T q / sqrt(d),
+      dE_act = sum_h dK'_h K_h^T,  dF_act = sum_h dV'_h V_h^T.
+    Inputs float64: q [Lq][H][d], K, V [L_act][H][d], o_s, d_out [Lq][H][d].
+    """
+    Lq, H, d = q.shape
+    r = E_act.shape[0]
+    x = np.einsum("thd,hd->th", q, w_g) + b_g[None, :]
+    g = gate(q, w_g, b_g)
+    o_l, k_low, v_low = linear_branch(q, K, V, E_act, F_act)
+    dx = np.einsum("thd,thd->th", d_out, o_s - o_l) * g * (1.0 - g)
+    d_wg = np.einsum("th,thd->hd", dx, q)
+    d_bg = dx.sum(axis=0)
+    dE = np.zeros_like(E_act)
+    dF = np.zeros_like(F_act)
+    dKl = np.empty((r, H, d))
+    dVl = np.empty((r, H, d))
+    for h in range(H):
+        dol = (1.0 - g[:, h])[:, None] * d_out[:, h, :]
+        logits = q[:, h, :] @ k_low[:, h, :].T / math.sqrt(d)
+        logits = logits - logits.max(axis=1, keepdims=True)
+        P = np.exp(logits)
+        P /= P.sum(axis=1, keepdims=True)
+        dV = P.T @ dol
+        dP = dol @ v_low[:, h, :].T
+        Dt = np.sum(dol * o_l[:, h, :], axis=1, keepdims=True)
+        dS = P * (dP - Dt)
+        dK = dS.T @ q[:, h, :] / math.sqrt(d)
+        dKl[:, h, :] = dK
+        dVl[:, h, :] = dV
+        dE += dK @ K[:, h, :].T
+        dF += dV @ V[:, h, :].T
+    del x
+    return {"d_wg": d_wg, "d_bg": d_bg, "d_E": dE, "d_F": dF, "d_klow": dKl, "d_vlow": dVl, "gate": g,
+            "o_linear": o_l}

@@ -127,6 +127,12 @@ MUTATIONS = [
     ("SplitMix64 with a wrong shift",
      "z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M", "z = ((z ^ (z >> 28)) * 0x94D049BB133111EB) & M",
      [pins.test_splitmix64_published_outputs]),
+    ("backward drops the softmax row term",
+     "        dS = P * (dP - Dt)", "        dS = P * dP",
+     [lambda: pins.test_backward_matches_finite_differences(11)]),
+    ("backward gates the low-rank gradient with g",
+     "        dol = (1.0 - g[:, h])[:, None] * d_out[:, h, :]", "        dol = g[:, h][:, None] * d_out[:, h, :]",
+     [lambda: pins.test_backward_matches_finite_differences(11)]),
     ("page summary sums instead of averaging",
      "return pool_k.mean(axis=1)", "return pool_k.sum(axis=1)",
      [pins.test_page_summary_closed_forms]),

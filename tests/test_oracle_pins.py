@@ -619,3 +619,60 @@ def test_random_policy_follows_its_keys():
     assert a == oracle.retrieve(kmean, prompts, 0, q, 3, "random", 7)[0].tolist()
     with pytest.raises(ValueError):
         oracle.retrieve(kmean, prompts, 0, q, 3, "nearest")
+
+
+# ---------------------------------------------------------------------------
+# backward of the learned parameters: finite differences of the loss
+# sum(d_out * O) through the forward's own gate, branch and fusion
+
+def _bwd_case(seed=11, Lq=9, H=2, d=4, L=7, r=3):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Lq, H, d))
+    K = rng.standard_normal((L, H, d))
+    V = rng.standard_normal((L, H, d))
+    E = rng.standard_normal((r, L)) / math.sqrt(L)
+    F = rng.standard_normal((r, L)) / math.sqrt(L)
+    w = rng.standard_normal((H, d)) / math.sqrt(d)
+    b = rng.standard_normal(H) * 0.3
+    o_s = rng.standard_normal((Lq, H, d)) * 0.1
+    d_out = rng.standard_normal((Lq, H, d))
+    return q, K, V, E, F, w, b, o_s, d_out
+
+
+def _loss(q, K, V, E, F, w, b, o_s, d_out):
+    o_l, _, _ = oracle.linear_branch(q, K, V, E, F)
+    return float(np.sum(d_out * oracle.fuse(oracle.gate(q, w, b), o_s, o_l)))
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_backward_matches_finite_differences(seed):
+    args = list(_bwd_case(seed))
+    got = oracle.backward_params(*args)
+    names = {3: "d_E", 4: "d_F", 5: "d_wg", 6: "d_bg"}
+    eps = 1e-6
+    for pos, name in names.items():
+        base = args[pos]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            up, dn = base.copy(), base.copy()
+            up[idx] += eps
+            dn[idx] -= eps
+            a_up, a_dn = list(args), list(args)
+            a_up[pos], a_dn[pos] = up, dn
+            num[idx] = (_loss(*a_up) - _loss(*a_dn)) / (2 * eps)
+        assert np.allclose(got[name], num, rtol=1e-6, atol=1e-8), name
+
+
+def test_backward_special_cases():
+    q, K, V, E, F, w, b, o_s, d_out = _bwd_case(14)
+    zero = oracle.backward_params(q, K, V, E, F, w, b, o_s, 0 * d_out)
+    for k in ("d_wg", "d_bg", "d_E", "d_F"):
+        assert np.array_equal(zero[k], 0 * zero[k])
+    # a saturated gate (g = 1): no gradient reaches the gate or the low-rank branch
+    sat = oracle.backward_params(q, K, V, E, F, 0 * w, np.full(len(b), 1e3), o_s, d_out)
+    for k in ("d_wg", "d_bg", "d_E", "d_F"):
+        assert np.all(sat[k] == 0)
+    # g = 1/2 exactly (w = b = 0): db = sum_t <d_out, O_s - O_l> / 4
+    half = oracle.backward_params(q, K, V, E, F, 0 * w, 0 * b, o_s, d_out)
+    want = np.einsum("thd,thd->h", d_out, o_s - half["o_linear"]) / 4.0
+    assert np.allclose(half["d_bg"], want, rtol=1e-13, atol=1e-14)
