@@ -286,6 +286,7 @@ HSAKV_API size_t hsakv_workspace_bytes(const hsakv_dims* dims, int32_t entry) {
         case HSAKV_ENTRY_FORWARD: return ws_forward(g, eb);
         case HSAKV_ENTRY_SUMMARY: return align_up(page_means_ws_bytes(g, g.P));
         case HSAKV_ENTRY_COMMIT: return align_up(page_means_ws_bytes(g, g.Lq / g.Tp + 1));
+        case HSAKV_ENTRY_BACKWARD: return align_up(backward_ws_bytes(g));
         default: return 0;
     }
 }
@@ -819,5 +820,30 @@ HSAKV_API int hkv_tier_apply(const hsakv_dims* dims, const hsakv_tiers* tiers, v
         }
     }
     if (n_upd > 0) launch_tier_table(tiers->page_slot, n_upd, upd_page, upd_value, st);
+    return done();
+}
+
+// ---- backward of the learned parameters ------------------------------------------
+
+HSAKV_API int hsa_backward_params(const hsakv_dims* dims, const void* q, const void* k_hist,
+                                  const void* v_hist, const void* k_intra, const void* v_intra,
+                                  const int32_t* n_sel, const float* w_g, const float* b_g,
+                                  const float* k_low, const float* v_low, const float* o_sparse,
+                                  const float* o_linear, const void* d_out, float* d_wg, float* d_bg,
+                                  float* d_E, float* d_F, void* ws, size_t ws_bytes, void* stream) {
+    HSAKV_CHECK(check_dims(dims));
+    HSAKV_REQUIRE(dims->dtype == HSAKV_BF16, HSAKV_ERR_BAD_DTYPE);
+    HSAKV_REQUIRE(q && k_hist && v_hist && k_intra && v_intra && n_sel && w_g && b_g && k_low && v_low &&
+                      o_sparse && o_linear && d_out && d_wg && d_bg && d_E && d_F,
+                  HSAKV_ERR_NULL_ARG);
+    HSAKV_REQUIRE(aligned(q) && aligned(k_hist) && aligned(v_hist) && aligned(k_intra) && aligned(v_intra) &&
+                      aligned(n_sel, 4) && aligned(w_g, 4) && aligned(b_g, 4) && aligned(k_low) &&
+                      aligned(v_low) && aligned(o_sparse) && aligned(o_linear) && aligned(d_out) &&
+                      aligned(d_wg, 4) && aligned(d_bg, 4) && aligned(d_E) && aligned(d_F),
+                  HSAKV_ERR_MISALIGNED);
+    const Geo g = make_geo(dims);
+    HSAKV_CHECK(check_ws(ws, ws_bytes, backward_ws_bytes(g)));
+    launch_backward_params(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low, v_low, o_sparse,
+                           o_linear, d_out, d_wg, d_bg, d_E, d_F, ws, (hipStream_t)stream);
     return done();
 }

@@ -49,13 +49,14 @@ ENTRY_LINEAR = 4
 ENTRY_FORWARD = 6
 ENTRY_SUMMARY = 7
 ENTRY_COMMIT = 8
+ENTRY_BACKWARD = 9
 
 EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",
     "hsakv_workspace_bytes", "hkv_page_summary", "hkv_gather", "hsa_select", "hsa_sparse_attn",
     "hsa_linear_branch", "hsa_fuse", "hsa_forward", "hsakv_fork_create", "hsakv_fork_destroy",
     "hsa_sparse_attn_static", "hkv_page_commit", "hsa_sparse_plan", "hsa_sparse_compute",
-    "hsakv_host_alloc", "hsakv_host_free", "hkv_tier_plan", "hkv_tier_apply",
+    "hsakv_host_alloc", "hsakv_host_free", "hkv_tier_plan", "hkv_tier_apply", "hsa_backward_params",
 ]
 
 
@@ -151,6 +152,7 @@ _sig = {
                               ctypes.POINTER(Fork)]),
     "hsakv_host_alloc": (c_int32, [c_size_t, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p)]),
     "hsakv_host_free": (c_int32, [_P]),
+    "hsa_backward_params": (c_int32, [_D] + [_P] * 18 + [c_size_t, _P]),
     "hkv_tier_plan": (c_int32, [c_int32, c_int32, _P, _P, _P, ctypes.c_int64, _P, c_int32, _P, _P, _P, _P, _P,
                                 _P]),
     "hkv_tier_apply": (c_int32, [_D, ctypes.POINTER(Tiers), _P, _P, c_int32, _P, _P, c_int32, _P, _P, c_int32,
@@ -355,6 +357,15 @@ def hsa_forward(dims: Dims, tau, cur_prompt: int, inputs: dict, outputs: dict, w
         ctypes.byref(dims), ctypes.cast(_host_f32(tau), c_void_p), int(cur_prompt),
         _retrieval(policy, seed), _tiers(tiers), ctypes.byref(ins), ctypes.byref(outs), w, wb,
         _stream(stream), ctypes.byref(fork) if fork is not None else None))
+
+
+def hsa_backward_params(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low, v_low,
+                        o_sparse, o_linear, d_out, d_wg, d_bg, d_E, d_F, ws, stream=None) -> None:
+    w, wb = _ws(ws)
+    _check("hsa_backward_params", _lib.hsa_backward_params(
+        ctypes.byref(dims), *[_ptr(x) for x in (q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low,
+                                                v_low, o_sparse, o_linear, d_out, d_wg, d_bg, d_E, d_F)],
+        w, wb, _stream(stream)))
 
 
 # ---- page tiers ---------------------------------------------------------------

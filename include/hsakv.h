@@ -97,6 +97,7 @@ extern "C" {
 #define HSAKV_ENTRY_FORWARD  6
 #define HSAKV_ENTRY_SUMMARY  7
 #define HSAKV_ENTRY_COMMIT   8   /* enough for a commit of up to Lq tokens */
+#define HSAKV_ENTRY_BACKWARD 9
 
 /* Sizes of one chunk-layer; all host integers. Supported: d in {64, 128};
  * Bq = 64; Binter and Bintra multiples of 64 up to 512; r a multiple of 32
@@ -387,6 +388,30 @@ int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
                 const hsakv_retrieval* retrieval, const hsakv_tiers* tiers,
                 const hsakv_inputs* in, hsakv_outputs* out, void* ws, size_t ws_bytes,
                 void* stream, const hsakv_fork* fork);
+
+/* Backward of the learned parameters (HSA paragraph: the branches are fused
+ * by learned gates, and the global branch is a Linformer-style projection
+ * with parameters E, F; the Linformer paper on the citation map). For an
+ * upstream gradient d_out = dLoss/dout (device, [Lq][H][d] bf16) of the
+ * chunk-layer's output, writes the gradients of the gate weights d_wg
+ * ([H][d] f32), biases d_bg ([H] f32) and of E and F, d_E and d_F ([r][L]
+ * f32, zero at the columns of absent slots). The sparse branch has no
+ * learned parameter and is held fixed. With g = sigmoid(<q, w_g[h]> +
+ * b_g[h]), dx = <d_out, o_sparse - o_linear> g (1 - g): d_wg[h] = sum_t dx q
+ * and d_bg[h] = sum_t dx; with dO_l = (1 - g) d_out and P = softmax(q K'^T /
+ * sqrt d): dV' = P^T dO_l, dK' = (P * (dO_l V'^T - <dO_l, o_linear>))^T q /
+ * sqrt d, d_E = sum_h dK'_h K_h^T and d_F = sum_h dV'_h V_h^T over the
+ * active keys. Inputs are the forward's: q, k_hist, v_hist, k_intra,
+ * v_intra, n_sel (device) as for hsa_linear_branch; w_g, b_g; k_low, v_low
+ * (K', V' from hsa_linear_branch, f32 [r][H][d]); o_sparse, o_linear (f32
+ * [Lq][H][d]). bf16 only (float32 data returns HSAKV_ERR_BAD_DTYPE).
+ * Workspace: HSAKV_ENTRY_BACKWARD. Every reduction runs in a fixed order:
+ * the results are the same bits from run to run. */
+int hsa_backward_params(const hsakv_dims* dims, const void* q, const void* k_hist, const void* v_hist,
+                        const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
+                        const float* b_g, const float* k_low, const float* v_low, const float* o_sparse,
+                        const float* o_linear, const void* d_out, float* d_wg, float* d_bg, float* d_E,
+                        float* d_F, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- page tiers ---- */
 

@@ -550,4 +550,4 @@ def backward_params(q: np.ndarray, K: np.ndarray, V: np.ndarray, E_act: np.ndarr
         dF += dV @ V[:, h, :].T
     del x
     return {"d_wg": d_wg, "d_bg": d_bg, "d_E": dE, "d_F": dF, "d_klow": dKl, "d_vlow": dVl, "gate": g,
-            "o_linear": o_l}
+            "o_linear": o_l, "k_low": k_low, "v_low": v_low}

@@ -19,6 +19,9 @@ Table 4). Values are synthetic stand-ins for real activations:
 * Linformer projections E, F ~ N(0, 1/L), L = Kp*Tp + Lq.
 * Gate weights w_g ~ N(0, 1/d), bias b_g = 0.
 * tau_h per head: alternating 0.35 / 1.0 for the tiny case, else U[tau_min, 1).
+* Upstream gradient of the output (backward cases) ~ N(0, 1) in the storage
+  type; a stand-in for the sparse branch's output, where the backward needs
+  one without running the sparse branch, ~ N(0, 1/4) in float32.
 
 bf16 tensors are drawn in float32 and rounded once, round-to-nearest-even,
 and returned as uint16 bit patterns. float32 tensors are returned as
@@ -46,6 +49,7 @@ __all__ = [
     "draw_chunk",
     "draw_tau",
     "page_prompts",
+    "draw_upstream",
 ]
 
 # Stream tags inside one workload seed.
@@ -53,6 +57,7 @@ _TAG_PAGE = 1
 _TAG_CHUNK = 2
 _TAG_TAU = 3
 _TAG_PROMPT = 4
+_TAG_UPSTREAM = 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -240,3 +245,13 @@ def draw_chunk(s: Shape) -> Dict[str, np.ndarray]:
         "q": q, "k_intra": k_intra, "v_intra": v_intra, "E": E, "F": F,
         "w_g": w_g, "b_g": b_g, "tau": draw_tau(s), "page_prompt": page_prompts(s),
     }
+
+
+def draw_upstream(s: Shape) -> Dict[str, np.ndarray]:
+    """Backward inputs: d_out [Lq][H][d] in the storage type (the upstream
+    gradient of the output) and o_sparse [Lq][H][d] float32 (a stand-in for
+    the sparse branch's output where a case does not run that branch)."""
+    rng = _rng(s, _TAG_UPSTREAM)
+    d_out = _store(_normal(rng, (s.Lq, s.H, s.d)), s.dtype)
+    o_sparse = _normal(rng, (s.Lq, s.H, s.d), 0.25).astype(np.float32)
+    return {"d_out": d_out, "o_sparse": o_sparse}

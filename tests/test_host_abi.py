@@ -151,6 +151,27 @@ def test_sparse_plan_and_compute_reject_before_launch():
     assert hs._lib.hsakv_last_hip_error() == 0
 
 
+def test_backward_rejects_before_launch():
+    d = _dims()
+    need = hs.workspace_bytes(d, hs.ENTRY_BACKWARD)
+    # gate partials, dO_l, 8 query slices of dK', dV' partials, sums and hi / lo parts
+    assert need >= 4 * d.Lq * d.H * d.d + 2 * 8 * d.r * d.H * d.d * 4
+    args = [FAKE] * 17
+    lib = hs._lib.hsa_backward_params
+    assert lib(ctypes.byref(_dims(dtype="f32")), *args, FAKE, need, None) == hs.ERR_BAD_DTYPE
+    assert lib(ctypes.byref(d), *args, FAKE, need - 1, None) == hs.ERR_WORKSPACE
+    assert lib(ctypes.byref(d), *args, FAKE + 16, need, None) == hs.ERR_WORKSPACE
+    for i in range(17):
+        a = list(args)
+        a[i] = None
+        assert lib(ctypes.byref(d), *a, FAKE, need, None) == hs.ERR_NULL_ARG, i
+    a = list(args)
+    a[9] = FAKE + 4      # k_low
+    assert lib(ctypes.byref(d), *a, FAKE, need, None) == hs.ERR_MISALIGNED
+    assert lib(ctypes.byref(_dims(d=96)), *args, FAKE, need, None) == hs.ERR_UNSUPPORTED
+    assert hs._lib.hsakv_last_hip_error() == 0
+
+
 def test_null_dims():
     assert hs._lib.hsakv_validate(None) == hs.ERR_NULL_ARG
 
