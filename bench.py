@@ -453,7 +453,9 @@ def stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops, ga
     entry_tflops = sparse_flops / (ms["sparse_attn"] * 1e-3) / 1e12
     gather_gbs = gather_bytes / (ms["gather"] * 1e-3) / 1e9
     traffic = recorded_traffic("hsa_sparse_attn", s.name)
+    bwd = backward_time(a, s, d, T, hs, torch, stream, k_hist, v_hist, n_sel, o_s)
     return {
+        "backward": bwd,
         "stages_ms": {k: round(v, 4) for k, v in ms.items()},
         "roofline": {"kernel": "k_sparse_attn32 + k_sparse_combine (hsa_sparse_compute: the attention over "
                                "the plan and the merge of split groups)",
@@ -468,6 +470,61 @@ def stage_times(a, s, d, T, page_kmean, tau, hs, torch, stream, sparse_flops, ga
                             "traffic": recorded_traffic("hkv_gather", s.name),
                             "algorithmic_bytes": gather_bytes},
     }
+
+
+def backward_time(a, s, d, T, hs, torch, stream, k_hist, v_hist, n_sel, o_s):
+    """hsa_backward_params on this chunk-layer's saved forward values and a
+    seeded upstream gradient; HIP events on the launch stream, mean over the
+    repetitions. Its floor is the larger of its algorithmic bytes over the
+    HBM peak and its algorithmic flops over the bf16 MFMA peak."""
+    import synth
+    if s.dtype != "bf16":
+        return None
+    dev = T["q"].device
+    up = synth.draw_upstream(s)
+    d_out = torch.from_numpy(up["d_out"].view(np.int16)).view(torch.bfloat16).to(dev)
+    o_l = torch.empty((s.Lq, s.H, s.d), dtype=torch.float32, device=dev)
+    k_low = torch.empty((s.r, s.H, s.d), dtype=torch.float32, device=dev)
+    v_low = torch.empty_like(k_low)
+    hs.hsa_linear_branch(d, T["q"], k_hist, v_hist, T["k_intra"], T["v_intra"], n_sel, T["E"], T["F"], o_l,
+                         k_low, v_low, torch.empty(hs.workspace_bytes(d, hs.ENTRY_LINEAR), dtype=torch.uint8,
+                                                   device=dev), stream=stream)
+    d_wg = torch.empty((s.H, s.d), dtype=torch.float32, device=dev)
+    d_bg = torch.empty((s.H,), dtype=torch.float32, device=dev)
+    d_E = torch.empty((s.r, s.L), dtype=torch.float32, device=dev)
+    d_F = torch.empty_like(d_E)
+    ws = torch.empty(hs.workspace_bytes(d, hs.ENTRY_BACKWARD), dtype=torch.uint8, device=dev)
+    fork = hs.fork_create()
+
+    def once():
+        hs.hsa_backward_params(d, T["q"], k_hist, v_hist, T["k_intra"], T["v_intra"], n_sel, T["w_g"], T["b_g"],
+                               k_low, v_low, o_s, o_l, d_out, d_wg, d_bg, d_E, d_F, ws, stream=stream, fork=fork)
+
+    once()
+    torch.cuda.synchronize()
+    reps = max(3, a.steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        once()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    hs.fork_destroy(fork)
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    ns = int(n_sel.item())
+    L_act = ns * s.Tp + s.Lq
+    HD = s.H * s.d
+    # dE = dK' K^T and dF = dV' V^T over the active keys, plus the low-rank
+    # backward (four r x d x Lq products per head) and the gate terms
+    flops = 2 * 2.0 * s.r * HD * L_act + 4 * 2.0 * s.r * s.d * s.Lq * s.H + 8.0 * s.Lq * HD
+    nbytes = (2.0 * L_act * HD * 2            # K and V rows of the active keys
+              + 2.0 * s.r * s.L * 4           # dE and dF
+              + s.Lq * HD * (2 + 2 + 4 + 4)   # q, d_out, o_sparse, o_linear
+              + 2.0 * s.r * HD * 4)           # K', V'
+    floor_us = max(nbytes / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+    return {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "floor_us": round(floor_us, 1), "frac": round(floor_us * 1e-3 / ms, 4),
+            "basis": "max(algorithmic bytes / 8 TB/s, algorithmic flops / 2.5 PFLOP/s bf16)"}
 
 
 # Sources whose kernels a recorded HBM-traffic figure covers; a figure is only

@@ -830,20 +830,32 @@ HSAKV_API int hsa_backward_params(const hsakv_dims* dims, const void* q, const v
                                   const int32_t* n_sel, const float* w_g, const float* b_g,
                                   const float* k_low, const float* v_low, const float* o_sparse,
                                   const float* o_linear, const void* d_out, float* d_wg, float* d_bg,
-                                  float* d_E, float* d_F, void* ws, size_t ws_bytes, void* stream) {
+                                  float* d_E, float* d_F, void* ws, size_t ws_bytes, void* stream,
+                                  const hsakv_fork* fork) {
     HSAKV_CHECK(check_dims(dims));
     HSAKV_REQUIRE(dims->dtype == HSAKV_BF16, HSAKV_ERR_BAD_DTYPE);
     HSAKV_REQUIRE(q && k_hist && v_hist && k_intra && v_intra && n_sel && w_g && b_g && k_low && v_low &&
                       o_sparse && o_linear && d_out && d_wg && d_bg && d_E && d_F,
                   HSAKV_ERR_NULL_ARG);
     HSAKV_REQUIRE(aligned(q) && aligned(k_hist) && aligned(v_hist) && aligned(k_intra) && aligned(v_intra) &&
-                      aligned(n_sel, 4) && aligned(w_g, 4) && aligned(b_g, 4) && aligned(k_low) &&
+                      aligned(n_sel, 4) && aligned(w_g) && aligned(b_g, 4) && aligned(k_low) &&
                       aligned(v_low) && aligned(o_sparse) && aligned(o_linear) && aligned(d_out) &&
                       aligned(d_wg, 4) && aligned(d_bg, 4) && aligned(d_E) && aligned(d_F),
                   HSAKV_ERR_MISALIGNED);
+    const bool split = fork && fork->stream;
+    HSAKV_REQUIRE(!split || (fork->fork && fork->join), HSAKV_ERR_NULL_ARG);
     const Geo g = make_geo(dims);
+    // the dE / dF kernel reads key rows through buffer resources of < 2^31 bytes
+    HSAKV_REQUIRE(g.L * g.HD * 2 < (1LL << 31), HSAKV_ERR_UNSUPPORTED);
     HSAKV_CHECK(check_ws(ws, ws_bytes, backward_ws_bytes(g)));
-    launch_backward_params(g, q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low, v_low, o_sparse,
-                           o_linear, d_out, d_wg, d_bg, d_E, d_F, ws, (hipStream_t)stream);
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e = launch_backward_params(
+        g, q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low, v_low, o_sparse, o_linear, d_out, d_wg,
+        d_bg, d_E, d_F, ws, st, split ? (hipStream_t)fork->stream : st,
+        split ? (hipEvent_t)fork->fork : nullptr, split ? (hipEvent_t)fork->join : nullptr);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return HSAKV_ERR_HIP;
+    }
     return done();
 }

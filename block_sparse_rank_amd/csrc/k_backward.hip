@@ -13,331 +13,703 @@
 //   dE = sum_h dK'_h K_h^T,  dF = sum_h dV'_h V_h^T
 // with E and F columns of absent history slots getting zero.
 //
-// Kernels (bf16 storage, float32 arithmetic):
-//   k_bwd_gate       one wave per (t, h): dx, dO_l, D
-//   k_bwd_gate_sum   one work-group per head: dw_g, db_g over tokens in a fixed order
-//   k_bwd_lse        one work-group per (head, 64 queries): log-sum-exp of each query's logits
-//   k_bwd_lowrank    one work-group per (head, 32 projected keys, query slice): partial dK', dV'
-//   k_bwd_lowrank_sum  partials added in slice order; dK', dV' also as bf16 hi + lo pairs
-//   k_bwd_proj       dE, dF = dK' K^T, dV' V^T on 32x32x16 bf16 MFMA (hi and lo products)
+// Every float32 operand of a bf16 MFMA product is split into hi = bf16(x)
+// and lo = bf16(x - hi), which keeps about 16 mantissa bits; q and the keys
+// and values are bf16 already. Every sum runs in a fixed order, so results
+// are the same bits from run to run.
+//
+// Kernels:
+//   k_bwd_gate        d / 8 lanes per (t, h): dx, D_t, dO_l as a hi + lo pair
+//   k_bwd_gate_part   per (head, token slice): partial dw_g, db_g
+//   k_bwd_gate_fin    per head: the slice partials in slice order
+//   k_bwd_split       K', V' -> hi + lo pairs
+//   k_bwd_lse         per (head, 256 queries): log2-sum-exp2 of each query's
+//                     scaled logits over the r projected keys (MFMA)
+//   k_bwd_lowrank     per (128 projected keys, head, query slice): partial
+//                     dK', dV' on MFMA, queries streamed through LDS
+//   k_bwd_lowrank_sum the slice partials in slice order -> dK', dV' hi + lo
+//   k_bwd_proj        dE, dF = dK' K^T, dV' V^T: 256 x 256 tiles, the
+//                     contraction over H d through a 3-stage LDS DMA ring
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
-constexpr int kSlices = 8;          // query slices of the low-rank backward
-constexpr int kKeyTile = 32;        // projected keys per work-group
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kGateSlices = 64;     // token slices of the gate-parameter sums
+constexpr int kKeyGroup = 128;      // projected keys per low-rank work-group (4 waves x 32)
+constexpr float kLog2e = 1.4426950408889634f;
 
 HSAKV_DEV float gate_of(float x) {
     const float z = expf(-fabsf(x));
     return x >= 0.f ? 1.0f / (1.0f + z) : z / (1.0f + z);
 }
 
-// One wave per (t, h); lanes take the head's columns e = lane, lane + 64.
+HSAKV_DEV void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+    hi = f32_to_bf16(x);
+    lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+HSAKV_DEV bf16x8_t ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+HSAKV_DEV bf16x8_t ld8(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+
+HSAKV_DEV f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- gate terms -------------------------------------------------------------
+
+// D / 8 lanes per (t, h), 8 columns each (16-byte loads); the dot products
+// are summed over those lanes by a fixed xor tree.
+template <int D>
 __global__ void __launch_bounds__(256)
 k_bwd_gate(Geo g, const bf16_t* __restrict__ q, const float* __restrict__ w_g, const float* __restrict__ b_g,
            const float* __restrict__ o_s, const float* __restrict__ o_l, const bf16_t* __restrict__ d_out,
-           float* __restrict__ dx, float* __restrict__ dol, float* __restrict__ Dt) {
-    const int lane = threadIdx.x & 63;
-    const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= (long long)g.Lq * g.H) return;
+           float* __restrict__ dx, bf16_t* __restrict__ dohi, bf16_t* __restrict__ dolo, float* __restrict__ Dt) {
+    constexpr int LP = D / 8, IPB = 256 / LP;     // lanes per item, items per work-group
+    const int sub = threadIdx.x % LP;
+    const long long n = (long long)g.Lq * g.H;
+    long long item = (long long)blockIdx.x * IPB + threadIdx.x / LP;
+    const bool ok = item < n;
+    item = ok ? item : n - 1;                     // every lane takes part in the shuffles
     const int h = (int)(item % g.H);
-    const long long base = item * g.d;            // (t * H + h) * d
+    const long long base = item * D + 8 * sub;    // (t * H + h) * d + 8 sub
+    float qv[8], dv[8], os[8], ol[8], wv[8];
+    Elt<bf16_t>::load8(q + base, qv);
+    Elt<bf16_t>::load8(d_out + base, dv);
+    Elt<float>::load8(o_s + base, os);
+    Elt<float>::load8(o_l + base, ol);
+    Elt<float>::load8(w_g + h * D + 8 * sub, wv);
     float xw = 0.f, dg = 0.f;
-    for (int e = lane; e < g.d; e += 64) {
-        xw = fmaf(bf16_to_f32(q[base + e]), w_g[h * g.d + e], xw);
-        dg = fmaf(bf16_to_f32(d_out[base + e]), o_s[base + e] - o_l[base + e], dg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        xw = fmaf(qv[e], wv[e], xw);
+        dg = fmaf(dv[e], os[e] - ol[e], dg);
     }
-    xw = wave_sum(xw);
-    dg = wave_sum(dg);
+#pragma unroll
+    for (int o = LP / 2; o >= 1; o >>= 1) {
+        xw += __shfl_xor(xw, o, 64);
+        dg += __shfl_xor(dg, o, 64);
+    }
     const float gv = gate_of(xw + b_g[h]);
     float dd = 0.f;
-    for (int e = lane; e < g.d; e += 64) {
-        const float v = (1.0f - gv) * bf16_to_f32(d_out[base + e]);
-        dol[base + e] = v;
-        dd = fmaf(v, o_l[base + e], dd);
+    bf16_t hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float v = (1.0f - gv) * dv[e];
+        split_bf16(v, hi[e], lo[e]);
+        dd = fmaf(v, ol[e], dd);
     }
-    dd = wave_sum(dd);
-    if (lane == 0) {
+#pragma unroll
+    for (int o = LP / 2; o >= 1; o >>= 1) dd += __shfl_xor(dd, o, 64);
+    if (!ok) return;
+    auto pack = [](const bf16_t* x) {
+        return uint4{x[0] | (uint32_t)x[1] << 16, x[2] | (uint32_t)x[3] << 16, x[4] | (uint32_t)x[5] << 16,
+                     x[6] | (uint32_t)x[7] << 16};
+    };
+    *reinterpret_cast<uint4*>(dohi + base) = pack(hi);
+    *reinterpret_cast<uint4*>(dolo + base) = pack(lo);
+    if (sub == 0) {
         dx[item] = dg * gv * (1.0f - gv);
         Dt[item] = dd;
     }
 }
 
-// dw_g[h][e] = sum_t dx[t][h] q[t][h][e], db_g[h] = sum_t dx[t][h]: 256
-// threads, column e = tid % d, token group tid / d takes t = grp, grp + G,
-// ...; the G group sums are added in group order.
+// Partial sums of dw_g[h][e] = sum_t dx[t][h] q[t][h][e] and db_g[h] over
+// the tokens of one slice: column e = tid % d, token group tid / d takes
+// every (256 / d)-th token of the slice; the groups are added in order.
 __global__ void __launch_bounds__(256)
-k_bwd_gate_sum(Geo g, const bf16_t* __restrict__ q, const float* __restrict__ dx, float* __restrict__ d_wg,
-               float* __restrict__ d_bg) {
-    __shared__ float pw[256], pb[256];
-    const int h = blockIdx.x;
+k_bwd_gate_part(Geo g, const bf16_t* __restrict__ q, const float* __restrict__ dx, float* __restrict__ pw,
+                float* __restrict__ pb) {
+    __shared__ float sw_[256], sb_[256];
+    const int h = blockIdx.x, slice = blockIdx.y;
     const int e = threadIdx.x % g.d, grp = threadIdx.x / g.d, G = 256 / g.d;
+    const int per = (g.Lq + kGateSlices - 1) / kGateSlices;
+    const int t0 = slice * per, t1 = t0 + per < g.Lq ? t0 + per : g.Lq;
     float sw = 0.f, sb = 0.f;
-    for (int t = grp; t < g.Lq; t += G) {
+    for (int t = t0 + grp; t < t1; t += G) {
         const float x = dx[(long long)t * g.H + h];
         sw = fmaf(x, bf16_to_f32(q[((long long)t * g.H + h) * g.d + e]), sw);
         sb += x;
     }
-    pw[threadIdx.x] = sw;
-    pb[threadIdx.x] = sb;
+    sw_[threadIdx.x] = sw;
+    sb_[threadIdx.x] = sb;
     __syncthreads();
     if (threadIdx.x < g.d) {
         float a = 0.f, b = 0.f;
         for (int k = 0; k < G; ++k) {
-            a += pw[k * g.d + threadIdx.x];
-            b += pb[k * g.d + threadIdx.x];
+            a += sw_[k * g.d + threadIdx.x];
+            b += sb_[k * g.d + threadIdx.x];
         }
-        d_wg[h * g.d + threadIdx.x] = a;
-        if (threadIdx.x == 0) d_bg[h] = b;
+        pw[((long long)slice * g.H + h) * g.d + threadIdx.x] = a;
+        if (threadIdx.x == 0) pb[slice * g.H + h] = b;
     }
 }
 
-// Log-sum-exp of q_t K'^T / sqrt d over the r projected keys: one
-// work-group per (head, 64 queries), 4 threads per query (a quarter of the
-// head's columns each, summed by lane shuffles), online max and sum.
+__global__ void __launch_bounds__(128)
+k_bwd_gate_fin(Geo g, const float* __restrict__ pw, const float* __restrict__ pb, float* __restrict__ d_wg,
+               float* __restrict__ d_bg) {
+    const int h = blockIdx.x, e = threadIdx.x;
+    if (e >= g.d) return;
+    float a = 0.f, b = 0.f;
+#pragma unroll 16
+    for (int s = 0; s < kGateSlices; ++s) {
+        a += pw[((long long)s * g.H + h) * g.d + e];
+        b += pb[s * g.H + h];
+    }
+    d_wg[h * g.d + e] = a;
+    if (e == 0) d_bg[h] = b;
+}
+
+// ---- low-rank branch ----------------------------------------------------------
+
+// K', V' (float32 [r][H][d]) -> hi + lo bf16 pairs, same layout.
+__global__ void __launch_bounds__(256)
+k_bwd_split(long long n, const float* __restrict__ kl, const float* __restrict__ vl, bf16_t* __restrict__ khi,
+            bf16_t* __restrict__ klo, bf16_t* __restrict__ vhi, bf16_t* __restrict__ vlo) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    split_bf16(kl[i], khi[i], klo[i]);
+    split_bf16(vl[i], vhi[i], vlo[i]);
+}
+
+// lse2[t][h] = log2 sum_j 2^(c s_j), c = log2(e) / sqrt(d), s_j = <q_t, K'_j>.
+// Work-group = 4 waves x 64 queries of one head (two 32-query tiles per
+// wave, so each K' fragment load serves two products). S^T = K' Q^T per
+// 32-key tile (A = K' hi, lo rows; B = the wave's queries, held in
+// registers); in the accumulator lane l holds query l % 32 of its tile and 16
+// of the tile's keys, lane l + 32 the other 16. Online max and sum per lane
+// pair.
 template <int D>
 __global__ void __launch_bounds__(256)
-k_bwd_lse(Geo g, const bf16_t* __restrict__ q, const float* __restrict__ k_low, float* __restrict__ lse) {
+k_bwd_lse(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo,
+          float* __restrict__ lse2) {
+    constexpr int KS = D / 16;
     const int h = blockIdx.y;
-    const int qi = threadIdx.x >> 2, quarter = threadIdx.x & 3;
-    const int t = blockIdx.x * 64 + qi;
-    constexpr int dq = D / 4;
-    const bool ok = t < g.Lq;
-    float qv[dq];
+    const int lane = threadIdx.x & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int qbase = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + l32;
+    bf16x8_t qf[2][KS];
 #pragma unroll
-    for (int k = 0; k < dq; ++k)
-        qv[k] = ok ? bf16_to_f32(q[((long long)t * g.H + h) * g.d + quarter * dq + k]) : 0.f;
-    const float scale = 1.0f / sqrtf((float)D);
-    float m = -INFINITY, l = 0.f;
-    for (int j = 0; j < g.r; ++j) {
-        const float* kr = k_low + ((long long)j * g.H + h) * g.d + quarter * dq;
-        float s = 0.f;
+    for (int u = 0; u < 2; ++u) {
+        const int query = qbase + 32 * u;
+        const bool ok = query < g.Lq;
+        const bf16_t* qp = q + (long long)(ok ? query : 0) * g.HD + h * D + 8 * g2;
 #pragma unroll
-        for (int k = 0; k < dq; ++k) s = fmaf(qv[k], kr[k], s);
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s *= scale;
-        const float mn = fmaxf(m, s);
-        l = l * expf(m - mn) + expf(s - mn);
-        m = mn;
+        for (int ks = 0; ks < KS; ++ks) qf[u][ks] = ok ? ld8(qp + 16 * ks) : bf16x8_t{};
     }
-    if (ok && quarter == 0) lse[(long long)t * g.H + h] = m + logf(l);
+    const float c = kLog2e / sqrtf((float)D);
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+    for (int j0 = 0; j0 < g.r; j0 += 32) {
+        const long long ko = (long long)(j0 + l32) * g.HD + h * D + 8 * g2;
+        f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t kh = ld8(khi + ko + 16 * ks), kl = ld8(klo + ko + 16 * ks);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                s[u] = mfma(kh, qf[u][ks], s[u]);
+                s[u] = mfma(kl, qf[u][ks], s[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float mx = s[u][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[u][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+            const float mn = fmaxf(m[u], mx);
+            float acc = l[u] * fast_exp2(m[u] - mn);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc += fast_exp2(fmaf(s[u][i], c, -mn));
+            l[u] = acc;
+            m[u] = mn;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float lt = l[u] + __shfl_xor(l[u], 32, 64);
+        const int query = qbase + 32 * u;
+        if (query < g.Lq && g2 == 0) lse2[(long long)query * g.H + h] = m[u] + __log2f(lt);
+    }
 }
 
-// Partial dK', dV' of 32 projected keys over one query slice: 256 threads =
-// 32 keys x 8 column groups (d / 8 columns each); per query the two dots are
-// summed over the 8 threads of a key by lane shuffles, in a fixed order.
+// LDS tile of 32 queries: Q, dO_l hi, dO_l lo rows (bf16, padded rows for the
+// transpose reads), then lse2 and D_t of the 32 queries.
+template <int D>
+struct BLay {
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int PITCH = 16 * (CPR + 4);      // bytes per LDS row
+    static constexpr int MAT = 32 * PITCH;
+    static constexpr int OFF_LSE = 3 * MAT, OFF_DT = 3 * MAT + 128;
+    static constexpr int BUF = 3 * MAT + 256;
+    static constexpr int KS = D / 16, DT = D / 32;
+    static constexpr int PER = 3 * 32 * CPR / 256;    // 16-byte chunks per thread and tile
+    static_assert(32 * CPR % 256 == 0, "each tile splits evenly over the 256 threads");
+};
+
+// Partial dK', dV' of 128 projected keys (4 waves x 32) of one head over one
+// slice of 32-query blocks. Per block, per wave:
+//   S  = Q K'^T, dP = dO_l V'^T             (A = query rows from LDS, B = key rows in registers)
+//   P  = 2^(c S - lse2), dS = P (dP - D) / sqrt d
+//   dV' += P^T dO_l,  dK' += dS^T Q          (A = P, dS from their own lanes, B by transpose reads)
+// In the S accumulator lane l holds key l % 32 and queries 8a + 4(l/32) + b
+// (a, b = 0..3); a 16-query chunk c of those registers is the A operand with
+// k order e < 4: query 16c + 4(l/32) + e, e >= 4: query 16c + 8 + 4(l/32) + e - 4,
+// and ds_read_b64_tr_b16 of the row-major Q and dO_l tiles gives the B
+// operand in the same query order. The next block's rows are loaded into
+// registers while the current one is computed, then written to the other
+// LDS buffer: one barrier per block.
 template <int D>
 __global__ void __launch_bounds__(256)
-k_bwd_lowrank(Geo g, const bf16_t* __restrict__ q, const float* __restrict__ k_low,
-              const float* __restrict__ v_low, const float* __restrict__ dol, const float* __restrict__ lse,
-              const float* __restrict__ Dt, float* __restrict__ pk, float* __restrict__ pv) {
+k_bwd_lowrank(Geo g, int nslices, const bf16_t* __restrict__ q, const bf16_t* __restrict__ dohi,
+              const bf16_t* __restrict__ dolo, const float* __restrict__ lse2, const float* __restrict__ Dt,
+              const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo, const bf16_t* __restrict__ vhi,
+              const bf16_t* __restrict__ vlo, float* __restrict__ pk, float* __restrict__ pv) {
+    using LY = BLay<D>;
+    __shared__ __attribute__((aligned(16))) char lds[2 * LY::BUF];
     const int h = blockIdx.y, slice = blockIdx.z;
-    const int jl = threadIdx.x >> 3, cg = threadIdx.x & 7;
-    const int j = blockIdx.x * kKeyTile + jl;
-    constexpr int dc = D / 8;
-    const bool ok = j < g.r;
-    const long long kro = ((long long)(ok ? j : 0) * g.H + h) * D + cg * dc;
-    float kj[dc], vj[dc], ak[dc], av[dc];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int G = lane >> 4, j = lane & 15;
+    const int key0 = blockIdx.x * kKeyGroup + 32 * wave;
+    const bool active = key0 < g.r;                   // whole wave: r is a multiple of 32
+    const int nqb = (g.Lq + 31) / 32;
+    const int per = (nqb + nslices - 1) / nslices;
+    const int b0 = slice * per, b1 = b0 + per < nqb ? b0 + per : nqb;
+
+    bf16x8_t kh[LY::KS], kl[LY::KS], vh[LY::KS], vl[LY::KS];
+    {
+        const long long ko = (long long)(active ? key0 + l32 : 0) * g.HD + h * D + 8 * g2;
 #pragma unroll
-    for (int k = 0; k < dc; ++k) {
-        kj[k] = k_low[kro + k];
-        vj[k] = v_low[kro + k];
-        ak[k] = 0.f;
-        av[k] = 0.f;
-    }
-    const float scale = 1.0f / sqrtf((float)D);
-    const int per = (g.Lq + kSlices - 1) / kSlices;
-    const int t0 = slice * per, t1 = t0 + per < g.Lq ? t0 + per : g.Lq;
-    for (int t = t0; t < t1; ++t) {
-        const long long ro = ((long long)t * g.H + h) * D + cg * dc;
-        float qv[dc], dv[dc];
-        float s = 0.f, dp = 0.f;
-#pragma unroll
-        for (int k = 0; k < dc; ++k) {
-            qv[k] = bf16_to_f32(q[ro + k]);
-            dv[k] = dol[ro + k];
-            s = fmaf(qv[k], kj[k], s);
-            dp = fmaf(dv[k], vj[k], dp);
-        }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        dp += __shfl_xor(dp, 1, 64);
-        dp += __shfl_xor(dp, 2, 64);
-        dp += __shfl_xor(dp, 4, 64);
-        const long long th = (long long)t * g.H + h;
-        const float p = expf(s * scale - lse[th]);
-        const float ds = p * (dp - Dt[th]) * scale;
-#pragma unroll
-        for (int k = 0; k < dc; ++k) {
-            av[k] = fmaf(p, dv[k], av[k]);
-            ak[k] = fmaf(ds, qv[k], ak[k]);
+        for (int ks = 0; ks < LY::KS; ++ks) {
+            kh[ks] = ld8(khi + ko + 16 * ks);
+            kl[ks] = ld8(klo + ko + 16 * ks);
+            vh[ks] = ld8(vhi + ko + 16 * ks);
+            vl[ks] = ld8(vlo + ko + 16 * ks);
         }
     }
-    if (!ok) return;
-    const long long o = (((long long)slice * g.r + j) * g.H + h) * D + cg * dc;
+    f32x16_t dk[LY::DT], dv[LY::DT];
 #pragma unroll
-    for (int k = 0; k < dc; ++k) {
-        pk[o + k] = ak[k];
-        pv[o + k] = av[k];
+    for (int dt = 0; dt < LY::DT; ++dt) {
+        dk[dt] = f32x16_t{};
+        dv[dt] = f32x16_t{};
     }
+
+    // staged chunks: matrix m (Q, dO_l hi, dO_l lo), row / chunk from tid + 256 v
+    constexpr int PM3 = LY::PER / 3;
+    const int Lq = g.Lq, HD = g.HD, H = g.H;
+    const bf16_t* const mats[3] = {q + h * D, dohi + h * D, dolo + h * D};
+    uint4 st[3][PM3];
+    float stl = 0.f;
+    auto gload = [&](int b) {
+        const int t0 = 32 * b;
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int v = 0; v < PM3; ++v) {
+                const int cidx = tid + 256 * v;
+                const int t = t0 + cidx / LY::CPR, ch = cidx % LY::CPR;
+                st[m][v] = t < Lq ? *reinterpret_cast<const uint4*>(mats[m] + (long long)t * HD + 8 * ch)
+                                  : uint4{0, 0, 0, 0};
+            }
+        if (tid < 64) {
+            const int t = t0 + (tid & 31);
+            // a query past Lq gets weight 2^-huge = 0 and D = 0
+            const float* src = tid < 32 ? lse2 : Dt;
+            stl = t < Lq ? src[(long long)t * H + h] : (tid < 32 ? 3.0e38f : 0.f);
+        }
+    };
+    auto swrite = [&](char* buf) {
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+            for (int v = 0; v < PM3; ++v) {
+                const int cidx = tid + 256 * v;
+                *reinterpret_cast<uint4*>(buf + m * LY::MAT + (cidx / LY::CPR) * LY::PITCH + 16 * (cidx % LY::CPR)) =
+                    st[m][v];
+            }
+        if (tid < 64) reinterpret_cast<float*>(buf + LY::OFF_LSE)[tid] = stl;
+    };
+
+    const float c = kLog2e / sqrtf((float)D);
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    auto compute = [&](const char* buf) {
+        f32x16_t s = {}, dp = {};
+        const char* arow = buf + l32 * LY::PITCH + 16 * g2;
+#pragma unroll
+        for (int ks = 0; ks < LY::KS; ++ks) {
+            const bf16x8_t a = ld8(arow + 32 * ks);
+            s = mfma(a, kh[ks], s);
+            s = mfma(a, kl[ks], s);
+            const bf16x8_t ah = ld8(arow + LY::MAT + 32 * ks);
+            const bf16x8_t al = ld8(arow + 2 * LY::MAT + 32 * ks);
+            dp = mfma(ah, vh[ks], dp);
+            dp = mfma(al, vh[ks], dp);
+            dp = mfma(ah, vl[ks], dp);
+        }
+        const float* ls = reinterpret_cast<const float*>(buf + LY::OFF_LSE);
+        const float* dd = reinterpret_cast<const float*>(buf + LY::OFF_DT);
+        bf16x8_t ph[2], pl[2], sh[2], sl[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int qi = 8 * (i >> 2) + 4 * g2 + (i & 3);
+            const float p = fast_exp2(fmaf(s[i], c, -ls[qi]));
+            const float ds = p * (dp[i] - dd[qi]) * inv_sqrt_d;
+            const __bf16 p_hi = (__bf16)p, s_hi = (__bf16)ds;
+            ph[i >> 3][i & 7] = p_hi;
+            pl[i >> 3][i & 7] = (__bf16)(p - (float)p_hi);
+            sh[i >> 3][i & 7] = s_hi;
+            sl[i >> 3][i & 7] = (__bf16)(ds - (float)s_hi);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int krow = 16 * cc + 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+            for (int dt = 0; dt < LY::DT; ++dt) {
+                const int off = krow * LY::PITCH + 2 * (32 * dt + 16 * (G & 1) + 4 * (j & 3));
+                bf16x8_t b[3];
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    const char* p = buf + m * LY::MAT + off;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 8 * LY::PITCH));
+                    b[m] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+                dv[dt] = mfma(ph[cc], b[1], dv[dt]);
+                dv[dt] = mfma(pl[cc], b[1], dv[dt]);
+                dv[dt] = mfma(ph[cc], b[2], dv[dt]);
+                dk[dt] = mfma(sh[cc], b[0], dk[dt]);
+                dk[dt] = mfma(sl[cc], b[0], dk[dt]);
+            }
+        }
+    };
+
+    if (b0 < b1) {
+        gload(b0);
+        swrite(lds);
+    }
+    __syncthreads();
+    for (int b = b0; b < b1; ++b) {
+        const int k = b - b0;
+        if (b + 1 < b1) gload(b + 1);
+        if (active) compute(lds + (k & 1) * LY::BUF);
+        if (b + 1 < b1) swrite(lds + ((k + 1) & 1) * LY::BUF);
+        __syncthreads();
+    }
+    if (!active) return;
+    // accumulator element i: key key0 + 8 (i / 4) + 4 g2 + i % 4, column 32 dt + l32
+#pragma unroll
+    for (int dt = 0; dt < LY::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+            const long long o = (((long long)slice * g.r + key) * g.H + h) * D + 32 * dt + l32;
+            pk[o] = dk[dt][i];
+            pv[o] = dv[dt][i];
+        }
 }
 
-// dK', dV' = sum of the slice partials in slice order; also stored as bf16
-// hi + lo pairs (hi = the rounded value, lo = the rounded remainder) for the
-// projection products.
+// dK', dV' = sum of the slice partials in slice order, as hi + lo pairs.
 __global__ void __launch_bounds__(256)
-k_bwd_lowrank_sum(long long n, const float* __restrict__ pk, const float* __restrict__ pv,
-                  float* __restrict__ dk, float* __restrict__ dv, bf16_t* __restrict__ khi, bf16_t* __restrict__ klo,
-                  bf16_t* __restrict__ vhi, bf16_t* __restrict__ vlo) {
+k_bwd_lowrank_sum(long long n, int nslices, const float* __restrict__ pk, const float* __restrict__ pv,
+                  bf16_t* __restrict__ khi, bf16_t* __restrict__ klo, bf16_t* __restrict__ vhi,
+                  bf16_t* __restrict__ vlo) {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     float a = 0.f, b = 0.f;
-#pragma unroll
-    for (int s = 0; s < kSlices; ++s) {
+    for (int s = 0; s < nslices; ++s) {
         a += pk[s * n + i];
         b += pv[s * n + i];
     }
-    if (dk) dk[i] = a;
-    if (dv) dv[i] = b;
-    const bf16_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
-    khi[i] = ah;
-    klo[i] = f32_to_bf16(a - bf16_to_f32(ah));
-    vhi[i] = bh;
-    vlo[i] = f32_to_bf16(b - bf16_to_f32(bh));
+    split_bf16(a, khi[i], klo[i]);
+    split_bf16(b, vhi[i], vlo[i]);
 }
 
+// ---- dE, dF --------------------------------------------------------------------
+
+constexpr int QM = 256, QN = 256, QK = 32;   // tile rows (of r), columns (of L), contraction step
+constexpr int Q_ROW = QK * 2;                // bytes per LDS row: 4 chunks of 16, XOR-swizzled
+constexpr int Q_AHI = 0, Q_ALO = QM * Q_ROW, Q_B = 2 * QM * Q_ROW;
+constexpr int Q_STAGE = 2 * QM * Q_ROW + QN * Q_ROW;   // 48 KiB: 48 DMA instructions of 1 KiB
+constexpr int Q_STAGES = 3;
+constexpr int Q_WAVES = 8;
+constexpr int Q_PER = Q_STAGE / 1024 / Q_WAVES;        // DMA instructions per wave and step
+static_assert(Q_PER * Q_WAVES * 1024 == Q_STAGE && Q_AHI + 16 * 1024 == Q_ALO && Q_ALO + 16 * 1024 == Q_B,
+              "instruction j of a step fills LDS bytes [1024 j, 1024 j + 1024) of its stage");
+
+// chunk ch of row m sits at slot ch ^ ((m >> 2) & 3): the 8 lanes of one
+// 128-byte LDS access (8 rows, one chunk each) hit distinct banks
+HSAKV_DEV int pslot(int m, int ch) { return m * Q_ROW + 16 * (ch ^ ((m >> 2) & 3)); }
+
+// Raw buffer resource over `bytes` from p (bytes < 2^31): loads past it read 0.
+HSAKV_DEV __amdgpu_buffer_rsrc_t q_rsrc(const bf16_t* p, long long bytes) {
+    const int n = bytes < 0 ? 0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), 0, n, 0x00020000);
+}
+
+// The LDS target of a DMA as a wave-uniform address the compiler cannot
+// trace to the ring (the kernel orders each DMA before the reads of its step
+// itself: a vmcnt wait, then the barrier).
+HSAKV_DEV __attribute__((address_space(3))) void* q_dst(char* p) {
+    const uint32_t v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+    return (__attribute__((address_space(3))) void*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
+}
+
+template <int N>
+HSAKV_DEV void q_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// LDS-only work-group barrier (DMA in flight stays in flight).
+HSAKV_DEV void q_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // dE (z = 0) or dF (z = 1) = dK' K_act^T (dV' V_act^T), written at the E/F
-// columns of the active keys, zeros at the columns of absent slots. One
-// work-group of 4 waves per (64 columns, 256 rows of r); wave w owns rows
-// 64 w .. 64 w + 63 of its row tile as 2 x 2 tiles of 32 x 32. The
-// contraction runs over the H d columns of the key rows, 16 at a time,
-// with the hi and lo parts of dK' as two products into one accumulator.
-// Operands are read straight from memory: A (dK' hi, lo rows) and B (key
-// rows, 16 bytes per lane) are 16-byte loads.
-__global__ void __launch_bounds__(256)
+// columns of the active keys, zeros at the columns of absent slots.
+// Work-group = 8 waves over a 256 x 256 tile (wave w: rows 64 (w % 4),
+// columns 128 (w / 4), 2 x 4 MFMA tiles). A tile's columns lie either in the
+// history part [0, Kp Tp) or in the chunk part [Kp Tp, L), so its key rows
+// come from one array: a history tile starting at or past the present rows
+// n_sel Tp is all zero. The contraction over the H d columns of the key rows
+// runs in 32-column steps through a 3-stage LDS ring filled by buffer-to-LDS
+// DMA (dK' hi, dK' lo, key rows; rows past r or past the tile's present keys
+// read as zero, and their products are zero), two steps in flight. The hi and lo parts of dK' are two
+// products into one accumulator.
+__global__ void __launch_bounds__(512, 1)
 k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
            const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
            const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo, const bf16_t* __restrict__ vhi,
            const bf16_t* __restrict__ vlo, float* __restrict__ dE, float* __restrict__ dF) {
+    __shared__ __attribute__((aligned(16))) char ring[Q_STAGES * Q_STAGE];
     const int z = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l32 = lane & 31, g2 = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
     int ns = *n_sel_p;
     ns = ns < 0 ? 0 : (ns > g.Kp ? g.Kp : ns);
     const long long Lh = (long long)ns * g.Tp;
-    const bf16_t* hist = z ? v_hist : k_hist;
-    const bf16_t* intra = z ? v_intra : k_intra;
-    const bf16_t* ahi = z ? vhi : khi;
-    const bf16_t* alo = z ? vlo : klo;
     float* out = z ? dF : dE;
-    const long long c0 = (long long)blockIdx.x * 64;
-    const int m0 = blockIdx.y * 256 + wave * 64;
-    // B rows: columns c0 + 32 nt + l32 of E/F -> a key row, or none
-    const bf16_t* brow[2];
-    bool bok[2];
-    for (int nt = 0; nt < 2; ++nt) {
-        const long long c = c0 + 32 * nt + l32;
-        bok[nt] = true;
-        if (c < Lh) brow[nt] = hist + c * g.HD;
-        else if (c >= g.hist_rows && c < g.L) brow[nt] = intra + (c - g.hist_rows) * g.HD;
-        else {
-            brow[nt] = hist;
-            bok[nt] = false;
+    const int nht = (int)((g.hist_rows + QN - 1) / QN);
+    const bool hist_tile = (int)blockIdx.x < nht;
+    const long long c0 = hist_tile ? (long long)blockIdx.x * QN : g.hist_rows + (long long)(blockIdx.x - nht) * QN;
+    const long long c_end = hist_tile ? (c0 + QN < g.hist_rows ? c0 + QN : g.hist_rows) : (c0 + QN < g.L ? c0 + QN : g.L);
+    const int m0 = blockIdx.y * QM;
+
+    if (hist_tile && c0 >= Lh) {
+        for (int i = tid; i < QM * QN; i += 512) {
+            const int m = m0 + i / QN;
+            const long long c = c0 + i % QN;
+            if (m < g.r && c < c_end) out[(long long)m * g.L + c] = 0.f;
         }
+        return;
     }
-    const bf16_t* arow_hi[2];
-    const bf16_t* arow_lo[2];
-    for (int mt = 0; mt < 2; ++mt) {
-        const int m = m0 + 32 * mt + l32;
-        const int mc = m < g.r ? m : g.r - 1;
-        arow_hi[mt] = ahi + (long long)mc * g.HD;
-        arow_lo[mt] = alo + (long long)mc * g.HD;
+
+    const bf16_t* keys = hist_tile ? (z ? v_hist : k_hist) + c0 * g.HD
+                                   : (z ? v_intra : k_intra) + (c0 - g.hist_rows) * g.HD;
+    const long long key_rows = (hist_tile ? (Lh < c_end ? Lh : c_end) : c_end) - c0;
+    const long long row_bytes = 2LL * g.HD;
+    const __amdgpu_buffer_rsrc_t rb = q_rsrc(keys, key_rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t rh = q_rsrc((z ? vhi : khi) + (long long)m0 * g.HD, (g.r - m0) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rl = q_rsrc((z ? vlo : klo) + (long long)m0 * g.HD, (g.r - m0) * row_bytes);
+
+    // Byte offsets of this wave's DMA instructions j = wave + 8 q: instruction
+    // j fills LDS rows 16 (j % 16) .. + 15 of matrix j / 16 (dK' hi, lo, keys);
+    // lane l fills slot l % 4 of row 16 (j % 16) + l / 4 with the chunk the
+    // swizzle puts there.
+    uint32_t off[Q_PER];
+#pragma unroll
+    for (int q = 0; q < Q_PER; ++q) {
+        const int j = wave + Q_WAVES * q;
+        const int row = 16 * (j & 15) + (lane >> 2);
+        const int ch = (lane & 3) ^ ((row >> 2) & 3);
+        off[q] = (uint32_t)(row * row_bytes + 16 * ch);
     }
-    f32x16_t acc[2][2];
+    const int nk = g.HD / QK;
+    auto send = [&](int st) __attribute__((always_inline)) {
+        if (st >= nk) return;
+        char* buf = ring + (st % Q_STAGES) * Q_STAGE;
+        const uint32_t koff = (uint32_t)st * QK * 2;
+#pragma unroll
+        for (int q = 0; q < Q_PER; ++q) {
+            const int j = wave + Q_WAVES * q;
+            const __amdgpu_buffer_rsrc_t rs = q < 2 ? rh : q < 4 ? rl : rb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, q_dst(buf + j * 1024), 16, off[q] + koff, 0, 0, 0);
+        }
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16_t{};
-    const bf16x8_t zero8 = {};
-#pragma unroll 4
-    for (int k0 = 0; k0 < g.HD; k0 += 16) {
-        const int ko = k0 + 8 * g2;
-        bf16x8_t a_hi[2], a_lo[2], b[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            a_hi[mt] = *reinterpret_cast<const bf16x8_t*>(arow_hi[mt] + ko);
-            a_lo[mt] = *reinterpret_cast<const bf16x8_t*>(arow_lo[mt] + ko);
-        }
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16_t{};
+    send(0);
+    send(1);
+#pragma unroll 1
+    for (int k = 0; k < nk; ++k) {
+        // step k has landed once only the step sent after it is outstanding
+        if (k + 1 < nk)
+            q_wait_vm<Q_PER>();
+        else
+            q_wait_vm<0>();
+        q_barrier();
+        send(k + 2);
+        const char* buf = ring + (k % Q_STAGES) * Q_STAGE;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) b[nt] = bok[nt] ? *reinterpret_cast<const bf16x8_t*>(brow[nt] + ko) : zero8;
+        for (int ks = 0; ks < QK / 16; ++ks) {
+            const int ch = 2 * ks + g2;
+            bf16x8_t ah[2], al[2], b[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi[mt], b[nt], acc[mt][nt], 0, 0, 0);
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo[mt], b[nt], acc[mt][nt], 0, 0, 0);
+            for (int mt = 0; mt < 2; ++mt) {
+                const int row = 64 * wm + 32 * mt + l32;
+                ah[mt] = ld8(buf + Q_AHI + pslot(row, ch));
+                al[mt] = ld8(buf + Q_ALO + pslot(row, ch));
             }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) b[nt] = ld8(buf + Q_B + pslot(128 * wn + 32 * nt + l32, ch));
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    acc[mt][nt] = mfma(ah[mt], b[nt], acc[mt][nt]);
+                    acc[mt][nt] = mfma(al[mt], b[nt], acc[mt][nt]);
+                }
+        }
     }
-    // element i of a 32 x 32 tile: row 8 (i / 4) + 4 g2 + i % 4, column l32
+
+    // accumulator element i: row 8 (i / 4) + 4 g2 + i % 4, column l32 of its tile
+#pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-        for (int nt = 0; nt < 2; ++nt) {
-            const long long c = c0 + 32 * nt + l32;
-            if (c >= g.L) continue;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const long long c = c0 + 128 * wn + 32 * nt + l32;
+            if (c >= c_end) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * g2 + (i & 3);
+                const int m = m0 + 64 * wm + 32 * mt + 8 * (i >> 2) + 4 * g2 + (i & 3);
                 if (m < g.r) out[(long long)m * g.L + c] = acc[mt][nt][i];
             }
         }
 }
 
-}  // namespace
-
-size_t backward_ws_bytes(const Geo& g) {
-    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t th = (size_t)g.Lq * g.H, rhd = (size_t)g.r * g.HD;
-    return al(th * 4) * 3 + al(th * g.d * 4) + 2 * al(kSlices * rhd * 4) + 2 * al(rhd * 4) + 4 * al(rhd * 2);
+// Query slices of the low-rank backward: about one work-group per CU of a
+// 256-CU part in total, a function of the sizes alone (so the summation
+// order, and the result bits, do not depend on the device).
+int lowrank_slices(const Geo& g) {
+    const int groups = (g.r + kKeyGroup - 1) / kKeyGroup * g.H;
+    const int nqb = (g.Lq + 31) / 32;
+    int s = 256 / groups;
+    s = s < 1 ? 1 : s;
+    return s < nqb ? s : nqb;
 }
 
-void launch_backward_params(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
-                            const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
-                            const float* b_g, const float* k_low, const float* v_low, const float* o_s,
-                            const float* o_l, const void* d_out, float* d_wg, float* d_bg, float* d_E, float* d_F,
-                            void* ws, hipStream_t st) {
+struct BwdWs {
+    float *dx, *Dt, *lse, *pw, *pb, *pk, *pv;
+    bf16_t *dohi, *dolo, *khf, *klf, *vhf, *vlf, *dkhi, *dklo, *dvhi, *dvlo;
+    size_t bytes;
+};
+
+// Workspace layout (each part 256-byte aligned); base null only sizes it.
+BwdWs carve(const Geo& g, void* base) {
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t th = (size_t)g.Lq * g.H, rhd = (size_t)g.r * g.HD;
-    char* p = (char*)ws;
-    float* dx = (float*)p; p += al(th * 4);
-    float* Dt = (float*)p; p += al(th * 4);
-    float* lse = (float*)p; p += al(th * 4);
-    float* dol = (float*)p; p += al(th * g.d * 4);
-    float* pk = (float*)p; p += al(kSlices * rhd * 4);
-    float* pv = (float*)p; p += al(kSlices * rhd * 4);
-    float* dk = (float*)p; p += al(rhd * 4);
-    float* dv = (float*)p; p += al(rhd * 4);
-    bf16_t* khi = (bf16_t*)p; p += al(rhd * 2);
-    bf16_t* klo = (bf16_t*)p; p += al(rhd * 2);
-    bf16_t* vhi = (bf16_t*)p; p += al(rhd * 2);
-    bf16_t* vlo = (bf16_t*)p;
+    const int ns = lowrank_slices(g);
+    char* p = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        char* r = p ? p + off : nullptr;
+        off += al(n);
+        return r;
+    };
+    BwdWs w;
+    w.dx = (float*)take(th * 4);
+    w.Dt = (float*)take(th * 4);
+    w.lse = (float*)take(th * 4);
+    w.pw = (float*)take((size_t)kGateSlices * g.H * g.d * 4);
+    w.pb = (float*)take((size_t)kGateSlices * g.H * 4);
+    w.dohi = (bf16_t*)take(th * g.d * 2);
+    w.dolo = (bf16_t*)take(th * g.d * 2);
+    w.khf = (bf16_t*)take(rhd * 2);
+    w.klf = (bf16_t*)take(rhd * 2);
+    w.vhf = (bf16_t*)take(rhd * 2);
+    w.vlf = (bf16_t*)take(rhd * 2);
+    w.pk = (float*)take((size_t)ns * rhd * 4);
+    w.pv = (float*)take((size_t)ns * rhd * 4);
+    w.dkhi = (bf16_t*)take(rhd * 2);
+    w.dklo = (bf16_t*)take(rhd * 2);
+    w.dvhi = (bf16_t*)take(rhd * 2);
+    w.dvlo = (bf16_t*)take(rhd * 2);
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
+size_t backward_ws_bytes(const Geo& g) { return carve(g, nullptr).bytes; }
+
+hipError_t launch_backward_params(const Geo& g, const void* q, const void* k_hist, const void* v_hist,
+                                  const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
+                                  const float* b_g, const float* k_low, const float* v_low, const float* o_s,
+                                  const float* o_l, const void* d_out, float* d_wg, float* d_bg, float* d_E,
+                                  float* d_F, void* ws, hipStream_t st, hipStream_t side, hipEvent_t ev_fork,
+                                  hipEvent_t ev_join) {
+    const BwdWs w = carve(g, ws);
+    const size_t th = (size_t)g.Lq * g.H, rhd = (size_t)g.r * g.HD;
     const bf16_t* qb = (const bf16_t*)q;
-    hipLaunchKernelGGL(k_bwd_gate, dim3((unsigned)((th + 3) / 4)), dim3(256), 0, st, g, qb, w_g, b_g, o_s, o_l,
-                       (const bf16_t*)d_out, dx, dol, Dt);
-    hipLaunchKernelGGL(k_bwd_gate_sum, dim3(g.H), dim3(256), 0, st, g, qb, (const float*)dx, d_wg, d_bg);
-    const dim3 lse_grid((g.Lq + 63) / 64, g.H), low_grid((g.r + kKeyTile - 1) / kKeyTile, g.H, kSlices);
-    if (g.d == 128) {
-        hipLaunchKernelGGL(k_bwd_lse<128>, lse_grid, dim3(256), 0, st, g, qb, k_low, lse);
-        hipLaunchKernelGGL(k_bwd_lowrank<128>, low_grid, dim3(256), 0, st, g, qb, k_low, v_low, (const float*)dol,
-                           (const float*)lse, (const float*)Dt, pk, pv);
-    } else {
-        hipLaunchKernelGGL(k_bwd_lse<64>, lse_grid, dim3(256), 0, st, g, qb, k_low, lse);
-        hipLaunchKernelGGL(k_bwd_lowrank<64>, low_grid, dim3(256), 0, st, g, qb, k_low, v_low, (const float*)dol,
-                           (const float*)lse, (const float*)Dt, pk, pv);
-    }
-    hipLaunchKernelGGL(k_bwd_lowrank_sum, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, st, (long long)rhd,
-                       (const float*)pk, (const float*)pv, dk, dv, khi, klo, vhi, vlo);
-    hipLaunchKernelGGL(k_bwd_proj, dim3((unsigned)((g.L + 63) / 64), (g.r + 255) / 256, 2), dim3(256), 0, st, g,
-                       (const bf16_t*)k_hist, (const bf16_t*)v_hist, (const bf16_t*)k_intra,
-                       (const bf16_t*)v_intra, n_sel, (const bf16_t*)khi, (const bf16_t*)klo,
-                       (const bf16_t*)vhi, (const bf16_t*)vlo, d_E, d_F);
+    const int ns = lowrank_slices(g);
+    const bool split = side != st;
+    hipError_t e = hipSuccess;
+    // the side stream starts once the inputs are ready on the main stream
+    if (split && (e = hipEventRecord(ev_fork, st)) == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+    if (e != hipSuccess) return e;
+
+    // side: K', V' split and the log-sum-exp (inputs only)
+    hipLaunchKernelGGL(k_bwd_split, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, side, (long long)rhd, k_low,
+                       v_low, w.khf, w.klf, w.vhf, w.vlf);
+    const dim3 lse_grid((g.Lq + 255) / 256, g.H), low_grid((g.r + kKeyGroup - 1) / kKeyGroup, g.H, ns);
+    if (g.d == 128)
+        hipLaunchKernelGGL(k_bwd_lse<128>, lse_grid, dim3(256), 0, side, g, qb, (const bf16_t*)w.khf,
+                           (const bf16_t*)w.klf, w.lse);
+    else
+        hipLaunchKernelGGL(k_bwd_lse<64>, lse_grid, dim3(256), 0, side, g, qb, (const bf16_t*)w.khf,
+                           (const bf16_t*)w.klf, w.lse);
+    if (split && (e = hipEventRecord(ev_join, side)) != hipSuccess) return e;
+
+    // main: the gate terms
+    if (g.d == 128)
+        hipLaunchKernelGGL(k_bwd_gate<128>, dim3((unsigned)((th + 15) / 16)), dim3(256), 0, st, g, qb, w_g, b_g, o_s,
+                           o_l, (const bf16_t*)d_out, w.dx, w.dohi, w.dolo, w.Dt);
+    else
+        hipLaunchKernelGGL(k_bwd_gate<64>, dim3((unsigned)((th + 31) / 32)), dim3(256), 0, st, g, qb, w_g, b_g, o_s,
+                           o_l, (const bf16_t*)d_out, w.dx, w.dohi, w.dolo, w.Dt);
+
+    // side: the gate-parameter sums, once dx is there
+    if (split && (e = hipEventRecord(ev_fork, st)) == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_bwd_gate_part, dim3(g.H, kGateSlices), dim3(256), 0, side, g, qb, (const float*)w.dx, w.pw,
+                       w.pb);
+    hipLaunchKernelGGL(k_bwd_gate_fin, dim3(g.H), dim3(128), 0, side, g, (const float*)w.pw, (const float*)w.pb,
+                       d_wg, d_bg);
+
+    // main: the low-rank backward after the log-sum-exp (the first join
+    // record), then dE and dF; the second join record covers the sums
+    if (split && (e = hipStreamWaitEvent(st, ev_join, 0)) == hipSuccess) e = hipEventRecord(ev_join, side);
+    if (e != hipSuccess) return e;
+    if (g.d == 128)
+        hipLaunchKernelGGL(k_bwd_lowrank<128>, low_grid, dim3(256), 0, st, g, ns, qb, (const bf16_t*)w.dohi,
+                           (const bf16_t*)w.dolo, (const float*)w.lse, (const float*)w.Dt, (const bf16_t*)w.khf,
+                           (const bf16_t*)w.klf, (const bf16_t*)w.vhf, (const bf16_t*)w.vlf, w.pk, w.pv);
+    else
+        hipLaunchKernelGGL(k_bwd_lowrank<64>, low_grid, dim3(256), 0, st, g, ns, qb, (const bf16_t*)w.dohi,
+                           (const bf16_t*)w.dolo, (const float*)w.lse, (const float*)w.Dt, (const bf16_t*)w.khf,
+                           (const bf16_t*)w.klf, (const bf16_t*)w.vhf, (const bf16_t*)w.vlf, w.pk, w.pv);
+    hipLaunchKernelGGL(k_bwd_lowrank_sum, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, st, (long long)rhd, ns,
+                       (const float*)w.pk, (const float*)w.pv, w.dkhi, w.dklo, w.dvhi, w.dvlo);
+    const unsigned tiles = (unsigned)((g.hist_rows + QN - 1) / QN + (g.Lq + QN - 1) / QN);
+    hipLaunchKernelGGL(k_bwd_proj, dim3(tiles, (g.r + QM - 1) / QM, 2), dim3(512), 0, st, g, (const bf16_t*)k_hist,
+                       (const bf16_t*)v_hist, (const bf16_t*)k_intra, (const bf16_t*)v_intra, n_sel,
+                       (const bf16_t*)w.dkhi, (const bf16_t*)w.dklo, (const bf16_t*)w.dvhi, (const bf16_t*)w.dvlo, d_E,
+                       d_F);
+    if (split) e = hipStreamWaitEvent(st, ev_join, 0);
+    return e;
 }

@@ -96,10 +96,13 @@ template <typename T>
 void launch_fuse(const Geo&, const void* q, const float* w_g, const float* b_g, const float* o_s,
                  const float* o_l, void* out, float* gate, hipStream_t);
 
-// Backward of the learned parameters (bf16): workspace of backward_ws_bytes(g) bytes.
+// Backward of the learned parameters (bf16): workspace of backward_ws_bytes(g)
+// bytes. With side != st part of the work runs on `side`, ordered by the two
+// events; returns the first failing event call's error (hipSuccess otherwise).
 size_t backward_ws_bytes(const Geo&);
-void launch_backward_params(const Geo&, const void* q, const void* k_hist, const void* v_hist, const void* k_intra,
-                            const void* v_intra, const int32_t* n_sel, const float* w_g, const float* b_g,
-                            const float* k_low, const float* v_low, const float* o_s, const float* o_l,
-                            const void* d_out, float* d_wg, float* d_bg, float* d_E, float* d_F, void* ws,
-                            hipStream_t);
+hipError_t launch_backward_params(const Geo&, const void* q, const void* k_hist, const void* v_hist,
+                                  const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
+                                  const float* b_g, const float* k_low, const float* v_low, const float* o_s,
+                                  const float* o_l, const void* d_out, float* d_wg, float* d_bg, float* d_E,
+                                  float* d_F, void* ws, hipStream_t st, hipStream_t side, hipEvent_t ev_fork,
+                                  hipEvent_t ev_join);

@@ -152,7 +152,7 @@ _sig = {
                               ctypes.POINTER(Fork)]),
     "hsakv_host_alloc": (c_int32, [c_size_t, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p)]),
     "hsakv_host_free": (c_int32, [_P]),
-    "hsa_backward_params": (c_int32, [_D] + [_P] * 18 + [c_size_t, _P]),
+    "hsa_backward_params": (c_int32, [_D] + [_P] * 18 + [c_size_t, _P, _P]),
     "hkv_tier_plan": (c_int32, [c_int32, c_int32, _P, _P, _P, ctypes.c_int64, _P, c_int32, _P, _P, _P, _P, _P,
                                 _P]),
     "hkv_tier_apply": (c_int32, [_D, ctypes.POINTER(Tiers), _P, _P, c_int32, _P, _P, c_int32, _P, _P, c_int32,
@@ -360,12 +360,12 @@ def hsa_forward(dims: Dims, tau, cur_prompt: int, inputs: dict, outputs: dict, w
 
 
 def hsa_backward_params(dims: Dims, q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low, v_low,
-                        o_sparse, o_linear, d_out, d_wg, d_bg, d_E, d_F, ws, stream=None) -> None:
+                        o_sparse, o_linear, d_out, d_wg, d_bg, d_E, d_F, ws, stream=None, fork=None) -> None:
     w, wb = _ws(ws)
     _check("hsa_backward_params", _lib.hsa_backward_params(
         ctypes.byref(dims), *[_ptr(x) for x in (q, k_hist, v_hist, k_intra, v_intra, n_sel, w_g, b_g, k_low,
                                                 v_low, o_sparse, o_linear, d_out, d_wg, d_bg, d_E, d_F)],
-        w, wb, _stream(stream)))
+        w, wb, _stream(stream), ctypes.byref(fork) if fork is not None else None))
 
 
 # ---- page tiers ---------------------------------------------------------------

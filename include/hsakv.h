@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HSAKV_VERSION 4
+#define HSAKV_VERSION 5
 
 /* status codes */
 #define HSAKV_OK                   0
@@ -402,16 +402,21 @@ int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
  * sqrt d): dV' = P^T dO_l, dK' = (P * (dO_l V'^T - <dO_l, o_linear>))^T q /
  * sqrt d, d_E = sum_h dK'_h K_h^T and d_F = sum_h dV'_h V_h^T over the
  * active keys. Inputs are the forward's: q, k_hist, v_hist, k_intra,
- * v_intra, n_sel (device) as for hsa_linear_branch; w_g, b_g; k_low, v_low
+ * v_intra, n_sel (device) as for hsa_linear_branch; w_g (16-byte aligned),
+ * b_g; k_low, v_low
  * (K', V' from hsa_linear_branch, f32 [r][H][d]); o_sparse, o_linear (f32
- * [Lq][H][d]). bf16 only (float32 data returns HSAKV_ERR_BAD_DTYPE).
- * Workspace: HSAKV_ENTRY_BACKWARD. Every reduction runs in a fixed order:
- * the results are the same bits from run to run. */
+ * [Lq][H][d]). bf16 only (float32 data returns HSAKV_ERR_BAD_DTYPE);
+ * (Kp Tp + Lq) H d 2 bytes must stay below 2^31 (else HSAKV_ERR_UNSUPPORTED).
+ * Workspace: HSAKV_ENTRY_BACKWARD. `fork` (host, nullable): with a fork
+ * whose stream is set, the log-sum-exp and the gate-parameter sums run on
+ * the fork's stream beside the gate terms and the low-rank backward; NULL
+ * runs everything on `stream`. Every reduction runs in a fixed order: the
+ * results are the same bits from run to run, with or without a fork. */
 int hsa_backward_params(const hsakv_dims* dims, const void* q, const void* k_hist, const void* v_hist,
                         const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
                         const float* b_g, const float* k_low, const float* v_low, const float* o_sparse,
                         const float* o_linear, const void* d_out, float* d_wg, float* d_bg, float* d_E,
-                        float* d_F, void* ws, size_t ws_bytes, void* stream);
+                        float* d_F, void* ws, size_t ws_bytes, void* stream, const hsakv_fork* fork);
 
 /* ---- page tiers ---- */
 

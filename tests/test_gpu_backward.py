@@ -32,7 +32,7 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import synth  # noqa: E402
 from block_sparse_rank_amd import hsakv as hs  # noqa: E402
-from gpu_util import Case, check_selection, dev, expected_sparse, host, ws  # noqa: E402
+from gpu_util import Case, check_selection, default_fork, dev, expected_sparse, host, ws  # noqa: E402
 
 STAGE = dict(rel=2e-5, max_rel=1e-4)
 E2E = dict(rel=1e-2, max_rel=2e-2)
@@ -87,14 +87,14 @@ def _active_cols(s, n_sel):
     return oracle.active_projection_columns(n_sel, s.Kp, s.Tp, s.Lq)
 
 
-def _backward(d, s, t, k_hist, v_hist, n_sel, k_low, v_low, o_s, o_l, d_out, w_g, b_g):
+def _backward(d, s, t, k_hist, v_hist, n_sel, k_low, v_low, o_s, o_l, d_out, w_g, b_g, fork=None):
     out = dict(d_wg=torch.full((s.H, s.d), float("nan"), device="cuda"),
                d_bg=torch.full((s.H,), float("nan"), device="cuda"),
                d_E=torch.full((s.r, s.L), float("nan"), device="cuda"),
                d_F=torch.full((s.r, s.L), float("nan"), device="cuda"))
     hs.hsa_backward_params(d, t["q"], k_hist, v_hist, t["k_intra"], t["v_intra"], n_sel, w_g, b_g,
                            k_low, v_low, o_s, o_l, d_out, out["d_wg"], out["d_bg"], out["d_E"], out["d_F"],
-                           ws(d, hs.ENTRY_BACKWARD))
+                           ws(d, hs.ENTRY_BACKWARD), fork=fork)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in out.items()}
 
@@ -150,10 +150,12 @@ def test_backward_stage_and_end_to_end(vid, s, kw, bg):
     got = _backward(c.d, s, c.t, t_kh, t_vh, t_ns, f32(want["k_low"]), f32(want["v_low"]),
                     f32(ref["o_sparse"]), f32(want["o_linear"]), t_do, c.t["w_g"], c.t["b_g"])
     _check(f"{vid} stage", s, got, want, n_sel, STAGE)
+    # a second call, on two streams (the fork): the same bits
     again = _backward(c.d, s, c.t, t_kh, t_vh, t_ns, f32(want["k_low"]), f32(want["v_low"]),
-                      f32(ref["o_sparse"]), f32(want["o_linear"]), t_do, c.t["w_g"], c.t["b_g"])
+                      f32(ref["o_sparse"]), f32(want["o_linear"]), t_do, c.t["w_g"], c.t["b_g"],
+                      fork=default_fork())
     for k in got:
-        assert got[k].tobytes() == again[k].tobytes(), f"{k}: not the same bits on a second call"
+        assert got[k].tobytes() == again[k].tobytes(), f"{k}: not the same bits with the fork"
 
     # end to end: the GPU forward's own saved values in
     km = c.page_summary()
@@ -204,5 +206,5 @@ def test_backward_wan13b_480p():
     print("[backward] wan1.3b-480p GPU", flush=True)
     got = _backward(c.d, s, c.t, dev(k_hist), dev(v_hist), dev(np.asarray([n_sel], np.int32)),
                     f32(want["k_low"]), f32(want["v_low"]), f32(up["o_sparse"]), f32(want["o_linear"]),
-                    dev(up["d_out"]), c.t["w_g"], c.t["b_g"])
+                    dev(up["d_out"]), c.t["w_g"], c.t["b_g"], fork=default_fork())
     _check("wan1.3b-480p stage", s, got, want, n_sel, STAGE)

@@ -38,7 +38,7 @@ def test_header_declares_exactly_the_exports():
 
 
 def test_version_and_status_strings():
-    assert hs.version() == 4
+    assert hs.version() == 5
     for code in range(-9, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
@@ -154,21 +154,33 @@ def test_sparse_plan_and_compute_reject_before_launch():
 def test_backward_rejects_before_launch():
     d = _dims()
     need = hs.workspace_bytes(d, hs.ENTRY_BACKWARD)
-    # gate partials, dO_l, 8 query slices of dK', dV' partials, sums and hi / lo parts
-    assert need >= 4 * d.Lq * d.H * d.d + 2 * 8 * d.r * d.H * d.d * 4
+    # gate partials, dO_l hi and lo, dK', dV' slice partials and hi / lo parts
+    assert need >= 3 * d.Lq * d.H * 4 + 2 * d.Lq * d.H * d.d * 2 + 2 * d.r * d.H * d.d * 4
     args = [FAKE] * 17
     lib = hs._lib.hsa_backward_params
-    assert lib(ctypes.byref(_dims(dtype="f32")), *args, FAKE, need, None) == hs.ERR_BAD_DTYPE
-    assert lib(ctypes.byref(d), *args, FAKE, need - 1, None) == hs.ERR_WORKSPACE
-    assert lib(ctypes.byref(d), *args, FAKE + 16, need, None) == hs.ERR_WORKSPACE
+    assert lib(ctypes.byref(_dims(dtype="f32")), *args, FAKE, need, None, None) == hs.ERR_BAD_DTYPE
+    assert lib(ctypes.byref(d), *args, FAKE, need - 1, None, None) == hs.ERR_WORKSPACE
+    assert lib(ctypes.byref(d), *args, FAKE + 16, need, None, None) == hs.ERR_WORKSPACE
     for i in range(17):
         a = list(args)
         a[i] = None
-        assert lib(ctypes.byref(d), *a, FAKE, need, None) == hs.ERR_NULL_ARG, i
+        assert lib(ctypes.byref(d), *a, FAKE, need, None, None) == hs.ERR_NULL_ARG, i
     a = list(args)
-    a[9] = FAKE + 4      # k_low
-    assert lib(ctypes.byref(d), *a, FAKE, need, None) == hs.ERR_MISALIGNED
-    assert lib(ctypes.byref(_dims(d=96)), *args, FAKE, need, None) == hs.ERR_UNSUPPORTED
+    a[8] = FAKE + 4      # k_low
+    assert lib(ctypes.byref(d), *a, FAKE, need, None, None) == hs.ERR_MISALIGNED
+    a = list(args)
+    a[6] = FAKE + 4      # w_g is read 16 bytes at a time
+    assert lib(ctypes.byref(d), *a, FAKE, need, None, None) == hs.ERR_MISALIGNED
+    assert lib(ctypes.byref(_dims(d=96)), *args, FAKE, need, None, None) == hs.ERR_UNSUPPORTED
+    # key rows of 2^31 bytes or more: (Kp Tp + Lq) H d 2 = (8 * 16384 + 4680) * 8192 * 2
+    big = _dims(H=64, Kp=8, tokens_per_frame=2048, Binter=512, r=32)
+    assert hs.validate(big) == hs.OK
+    assert lib(ctypes.byref(big), *args, FAKE, hs.workspace_bytes(big, hs.ENTRY_BACKWARD), None, None) == \
+        hs.ERR_UNSUPPORTED
+    # a fork with a stream needs both events
+    half = hs.Fork()
+    half.stream = FAKE
+    assert lib(ctypes.byref(d), *args, FAKE, need, None, ctypes.byref(half)) == hs.ERR_NULL_ARG
     assert hs._lib.hsakv_last_hip_error() == 0
 
 
