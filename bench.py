@@ -303,72 +303,104 @@ def commit_time(a, s, T, hs, torch, stream):
 
 
 def sweep_tiers(a):
-    """Tiered pages on the Wan-1.3B 480p chunk-layer: every page in the pinned
-    host store, 8 HBM slots. Times the forward with the retrieved pages all in
-    HBM slots (after the planner promoted them) and with none (read from the
-    host store over the bus), the promotion itself, and the HBM the pool takes
-    against the history it serves."""
+    """Tiered pages: every page in the pinned host store, 8 HBM slots, on the
+    Wan-1.3B 480p chunk-layer at two horizons (32 and 96 pages of history).
+    Per horizon: the forward with the whole pool in HBM (reference), with
+    the retrieved pages read from the host store over the bus, and with them
+    in HBM slots after the planner promoted them; the promotion itself; and
+    the forward while another page is promoted on a second stream (the
+    prefetch of a page the next chunk-layer retrieves). HBM held by the pool
+    stays at the slots whatever the horizon."""
     import torch
 
     import synth
     from block_sparse_rank_amd import hsakv as hs
-    s = synth.shape("wan1.3b-480p")
-    run = time_forward(s, 2, 1)           # uploads the chunk-layer; its all-HBM times are the reference
-    d, T, stream = run["d"], run["T"], run["stream"]
-    slots = 8
-    hk = hs.HostStore(run["pool_k"].shape, run["pool_k"].dtype)
-    hv = hs.HostStore(run["pool_v"].shape, run["pool_v"].dtype)
-    hk.array[:] = run["pool_k"]
-    hv.array[:] = run["pool_v"]
-    pk = torch.zeros((slots, s.Tp, s.H, s.d), dtype=T["q"].dtype, device=T["q"].device)
-    pv = torch.zeros_like(pk)
-    table = torch.full((s.P,), -1, dtype=torch.int32, device=pk.device)
-    tiers = hs.Tiers(table.data_ptr(), hk.device, hv.device)
-    pl = hs.TierPlacement(s.P, slots)
-    outs = {"out": torch.empty((s.Lq, s.H, s.d), dtype=T["q"].dtype, device=pk.device),
-            "n_sel": run["n_sel"], "page_idx": torch.empty(s.Kp, dtype=torch.int32, device=pk.device)}
-    ins = {k: T[k] for k in ("q", "k_intra", "v_intra", "E", "F", "w_g", "b_g", "page_prompt")}
-    ins.update(pool_k=pk, pool_v=pv, page_kmean=run["page_kmean"])
-    ws = torch.empty(hs.workspace_bytes(d, hs.ENTRY_FORWARD), dtype=torch.uint8, device=pk.device)
+    for name in ("wan1.3b-480p", "wan1.3b-480p-60s"):
+        s = synth.shape(name)
+        run = time_forward(s, 2, 1)       # uploads the chunk-layer; its all-HBM times are the reference
+        d, T, stream = run["d"], run["T"], run["stream"]
+        del T["pool_k"], T["pool_v"]      # the pool now lives in host memory only
+        torch.cuda.empty_cache()
+        slots = 8
+        hk = hs.HostStore(run["pool_k"].shape, run["pool_k"].dtype)
+        hv = hs.HostStore(run["pool_v"].shape, run["pool_v"].dtype)
+        hk.array[:] = run["pool_k"]
+        hv.array[:] = run["pool_v"]
+        pk = torch.zeros((slots, s.Tp, s.H, s.d), dtype=T["q"].dtype, device=T["q"].device)
+        pv = torch.zeros_like(pk)
+        table = torch.full((s.P,), -1, dtype=torch.int32, device=pk.device)
+        tiers = hs.Tiers(table.data_ptr(), hk.device, hv.device)
+        pl = hs.TierPlacement(s.P, slots)
+        outs = {"out": torch.empty((s.Lq, s.H, s.d), dtype=T["q"].dtype, device=pk.device),
+                "n_sel": run["n_sel"], "page_idx": torch.empty(s.Kp, dtype=torch.int32, device=pk.device)}
+        ins = {k: T[k] for k in ("q", "k_intra", "v_intra", "E", "F", "w_g", "b_g", "page_prompt")}
+        ins.update(pool_k=pk, pool_v=pv, page_kmean=run["page_kmean"])
+        ws = torch.empty(hs.workspace_bytes(d, hs.ENTRY_FORWARD), dtype=torch.uint8, device=pk.device)
 
-    def timed(fn, reps):
-        fn()
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(reps):
+                fn()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            return e[0].elapsed_time(e[1]) / reps
+
+        fwd = lambda: hs.hsa_forward(d, run["tau"], s.cur_prompt, ins, outs, ws, stream=stream,  # noqa: E731
+                                     fork=run["fork"], tiers=tiers)
+        miss_ms = timed(fwd, max(2, a.steps // 4))
         torch.cuda.synchronize()
+        n = int(outs["n_sel"].cpu()[0])
+        pages = outs["page_idx"].cpu().tolist()[:n]
+        pp, ps, up, uv = hs.hkv_tier_plan(pl, 1, pages)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record(stream)
-        for _ in range(reps):
-            fn()
+        hs.hkv_tier_apply(d, tiers, pk, pv, slots, pp, ps, up, uv, stream=stream)
         e[1].record(stream)
         torch.cuda.synchronize()
-        return e[0].elapsed_time(e[1]) / reps
+        apply_ms = e[0].elapsed_time(e[1])
+        hit_ms = timed(fwd, a.steps)
 
-    fwd = lambda: hs.hsa_forward(d, run["tau"], s.cur_prompt, ins, outs, ws, stream=stream,  # noqa: E731
-                                 fork=run["fork"], tiers=tiers)
-    miss_ms = timed(fwd, max(2, a.steps // 4))
-    torch.cuda.synchronize()
-    n = int(outs["n_sel"].cpu()[0])
-    pages = outs["page_idx"].cpu().tolist()[:n]
-    pp, ps, up, uv = hs.hkv_tier_plan(pl, 1, pages)
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e[0].record(stream)
-    hs.hkv_tier_apply(d, tiers, pk, pv, slots, pp, ps, up, uv, stream=stream)
-    e[1].record(stream)
-    torch.cuda.synchronize()
-    apply_ms = e[0].elapsed_time(e[1])
-    hit_ms = timed(fwd, a.steps)
-    page_bytes = 2 * s.Tp * s.H * s.d * 2
-    line = {"sweep": "tiers", "workload": s.name, "P": s.P, "hbm_slots": slots, "retrieved": pages,
-            "forward_all_hbm_pool_ms": round(run["warm_ms"], 4),
-            "forward_pages_in_hbm_slots_ms": round(hit_ms, 4),
-            "forward_pages_from_host_store_ms": round(miss_ms, 4),
-            "promote_pages_ms": round(apply_ms, 4), "promoted": len(pp),
-            "promote_GBps": round(len(pp) * page_bytes / (apply_ms * 1e-3) / 1e9, 1),
-            "hbm_pool_bytes": slots * page_bytes, "history_bytes": s.P * page_bytes}
-    hs.fork_destroy(run["fork"])
-    torch.cuda.synchronize()
-    hk.free()
-    hv.free()
-    print(json.dumps(line), flush=True)
+        # one more page promoted on a second stream while the forward runs:
+        # the planner evicts the least recently used slot, never a page of
+        # the forward (those were used last)
+        side = torch.cuda.Stream()
+        others = [p for p in range(s.P) if p not in pages]
+        reps = max(3, a.steps // 2)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for k in range(reps):
+            extra = others[k % len(others)]
+            pp2, ps2, up2, uv2 = hs.hkv_tier_plan(pl, 2 + k, pages + [extra])
+            assert len(pp2) == 1 and pp2[0] == extra
+            ev[k][0].record(side)
+            hs.hkv_tier_apply(d, tiers, pk, pv, slots, pp2, ps2, up2, uv2, stream=side)
+            ev[k][1].record(side)
+            ev[k][2].record(stream)
+            fwd()
+            ev[k][3].record(stream)
+            torch.cuda.synchronize()
+        fwd_beside_ms = sum(ev[k][2].elapsed_time(ev[k][3]) for k in range(reps)) / reps
+        promote1_ms = sum(ev[k][0].elapsed_time(ev[k][1]) for k in range(reps)) / reps
+        page_bytes = 2 * s.Tp * s.H * s.d * 2
+        line = {"sweep": "tiers", "workload": s.name, "P": s.P, "hbm_slots": slots, "retrieved": pages,
+                "forward_all_hbm_pool_ms": round(run["warm_ms"], 4),
+                "forward_pages_in_hbm_slots_ms": round(hit_ms, 4),
+                "forward_pages_from_host_store_ms": round(miss_ms, 4),
+                "promote_pages_ms": round(apply_ms, 4), "promoted": len(pp),
+                "promote_GBps": round(len(pp) * page_bytes / (apply_ms * 1e-3) / 1e9, 1),
+                "forward_beside_one_page_promotion_ms": round(fwd_beside_ms, 4),
+                "one_page_promotion_beside_forward_ms": round(promote1_ms, 4),
+                "hbm_pool_bytes": slots * page_bytes, "history_bytes": s.P * page_bytes}
+        hs.fork_destroy(run["fork"])
+        torch.cuda.synchronize()
+        hk.free()
+        hv.free()
+        del run, pk, pv, ins, outs, ws
+        torch.cuda.empty_cache()
+        print(json.dumps(line), flush=True)
     return 0
 
 
@@ -530,10 +562,8 @@ def backward_time(a, s, d, T, hs, torch, stream, k_hist, v_hist, n_sel, o_s):
 # Sources whose kernels a recorded HBM-traffic figure covers; a figure is only
 # reported while the hash of these files matches the one recorded with it.
 TRAFFIC_SOURCES = {
-    "hsa_sparse_attn": ["block_sparse_rank_amd/csrc/k_sparse32.hip", "block_sparse_rank_amd/csrc/common.h",
-                        "block_sparse_rank_amd/csrc/launch.h"],
-    "hkv_gather": ["block_sparse_rank_amd/csrc/k_hkv.hip", "block_sparse_rank_amd/csrc/common.h",
-                   "block_sparse_rank_amd/csrc/launch.h"],
+    "hsa_sparse_attn": ["block_sparse_rank_amd/csrc/k_sparse32.hip", "block_sparse_rank_amd/csrc/common.h"],
+    "hkv_gather": ["block_sparse_rank_amd/csrc/k_hkv.hip", "block_sparse_rank_amd/csrc/common.h"],
 }
 
 

@@ -19,7 +19,7 @@ retrieval is what is used. The Linformer paper (cited on the mlsanity map)
 defines the low-rank projection.
 
 The pages give no equations. Every step below states the reading it takes
-where they are silent; the readings are numbered R1..R20 and listed, with
+where they are silent; the readings are numbered R1..R28 and listed, with
 reasons, in the design notes of this repository.
 
 Decision precision. Page ranking and block selection turn floating point
