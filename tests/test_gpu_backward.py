@@ -172,14 +172,15 @@ def test_backward_stage_and_end_to_end(vid, s, kw, bg):
 
 
 @pytest.mark.timeout(900)
-def test_backward_wan13b_480p():
-    """Wan-1.3B-shaped 480p (H = 12, d = 128, Lq = 4680, four 12480-token
-    slots, r = 256) at the stage bar. The history cache comes from the
-    oracle's own retrieval; the sparse branch's output is the seeded
-    stand-in (the backward holds it fixed, so any values exercise the same
-    arithmetic)."""
-    s = synth.shape("wan1.3b-480p")
-    print("[backward] wan1.3b-480p generating", flush=True)
+@pytest.mark.parametrize("name", ["wan1.3b-480p", "wan14b-480p"])
+def test_backward_full_shape(name):
+    """Wan-1.3B- and Wan-14B-shaped 480p (H = 12 or 40, d = 128, Lq = 4680,
+    four 12480-token slots, r = 256) at the stage bar, every element of every
+    gradient. The history cache comes from the oracle's own retrieval; the
+    sparse branch's output is the seeded stand-in (the backward holds it
+    fixed, so any values exercise the same arithmetic)."""
+    s = synth.shape(name)
+    print(f"[backward] {name} generating", flush=True)
     c = Case(s)
     ch = c.ch
     up = synth.draw_upstream(s)
@@ -194,7 +195,7 @@ def test_backward_wan13b_480p():
     E_act = oracle.as_f64(ch["E"], s.dtype)[:, cols]
     F_act = oracle.as_f64(ch["F"], s.dtype)[:, cols]
     o_s = up["o_sparse"].astype(np.float64)
-    print("[backward] wan1.3b-480p oracle", flush=True)
+    print(f"[backward] {name} oracle", flush=True)
     want = oracle.backward_params(qf, K, V, E_act, F_act, np.asarray(ch["w_g"], np.float64),
                                   np.asarray(ch["b_g"], np.float64), o_s, oracle.as_f64(up["d_out"], s.dtype))
     del K, V
@@ -203,8 +204,8 @@ def test_backward_wan13b_480p():
     k_hist[:n_sel * s.Tp] = kh
     v_hist[:n_sel * s.Tp] = vh
     f32 = lambda a: dev(np.ascontiguousarray(a, np.float32))  # noqa: E731
-    print("[backward] wan1.3b-480p GPU", flush=True)
+    print(f"[backward] {name} GPU", flush=True)
     got = _backward(c.d, s, c.t, dev(k_hist), dev(v_hist), dev(np.asarray([n_sel], np.int32)),
                     f32(want["k_low"]), f32(want["v_low"]), f32(up["o_sparse"]), f32(want["o_linear"]),
                     dev(up["d_out"]), c.t["w_g"], c.t["b_g"], fork=default_fork())
-    _check("wan1.3b-480p stage", s, got, want, n_sel, STAGE)
+    _check(f"{name} stage", s, got, want, n_sel, STAGE)
