@@ -741,7 +741,8 @@ HSAKV_API int hkv_tier_plan(int32_t P, int32_t slots, int32_t* slot_of_page, int
                             int64_t* last_use, int64_t now, const int32_t* want, int32_t n_want,
                             int32_t* promote_page, int32_t* promote_slot, int32_t* n_promote,
                             int32_t* upd_page, int32_t* upd_value, int32_t* n_upd) {
-    if (!slot_of_page || !page_of_slot || !last_use || (n_want > 0 && !want) || !promote_page ||
+    // with no slots there is no page_of_slot to pass, and nothing is promoted
+    if (!slot_of_page || (slots > 0 && !page_of_slot) || !last_use || (n_want > 0 && !want) || !promote_page ||
         !promote_slot || !n_promote || !upd_page || !upd_value || !n_upd)
         return HSAKV_ERR_NULL_ARG;
     if (P < 1 || slots < 0 || n_want < 0) return HSAKV_ERR_BAD_DIMS;

@@ -427,7 +427,8 @@ int hsakv_host_alloc(size_t bytes, void** host_ptr, void** device_ptr);
 int hsakv_host_free(void* host_ptr);
 
 /* Host-only least-recently-used planner of the HBM slots; touches no GPU.
- * slot_of_page [P] (slot or -1), page_of_slot [slots] (page or -1) and
+ * slot_of_page [P] (slot or -1), page_of_slot [slots] (page or -1; may be
+ * NULL when slots is 0) and
  * last_use [P] are the caller's host copy of the placement, updated in
  * place. The n_want pages of `want` (e.g. the pages the last forwards
  * retrieved, then the newest pages) get last_use = now; each one not in a
