@@ -107,7 +107,9 @@ def main() -> int:
                                "(cold MALL and L2)",
                    "median_ms": round(ms_med, 4), "p10_ms": round(ms_p10, 4),
                    "p90_ms": round(ms_p90, 4), "warm_mean_ms": round(warm_ms, 4),
-                   "wall_ms_per_step_incl_flush": round(wall_ms, 4)},
+                   "wall_ms_per_step_incl_flush": round(wall_ms, 4),
+                   "graph_replay_median_ms": round(run["graph_ms_med"], 4),
+                   "graph_replay_warm_mean_ms": round(run["graph_warm_ms"], 4)},
         "forward_roofline": {"floor_us": round(floor_us, 1),
                              "frac": round(floor_us * 1e-3 / ms_med, 4),
                              "floor_parts_us": {k: round(v, 1) for k, v in floor_parts.items()},
@@ -202,11 +204,35 @@ def time_forward(s, steps, warmup, policy="two_stage", seed=0):
     ev[1].record(stream)
     torch.cuda.synchronize()
     warm_ms = ev[0].elapsed_time(ev[1]) / steps
+    # the same step captured once in a HIP graph and replayed: same protocol
+    # (1 GiB written before each replay, outside the events), then back to back
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        hs.hsa_forward(d, tau, s.cur_prompt, ins, outs, ws_fwd, stream=cap, fork=fork, policy=policy, seed=seed)
+    torch.cuda.synchronize()
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(steps):
+        flush.fill_(k & 0xff)
+        gevs[k][0].record(stream)
+        graph.replay()
+        gevs[k][1].record(stream)
+    torch.cuda.synchronize()
+    gcold = np.array([e0.elapsed_time(e1) for e0, e1 in gevs])
+    ev[0].record(stream)
+    for _ in range(steps):
+        graph.replay()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    graph_warm_ms = ev[0].elapsed_time(ev[1]) / steps
+    del graph
     del flush
     return {"d": d, "T": T, "ch": ch, "pool_k": pool_k, "pool_v": pool_v, "page_kmean": page_kmean,
             "tau": tau, "stream": stream, "fork": fork, "n_sel": n_sel, "sel_count": sel_count,
             "sel_idx": sel_idx, "ms_med": ms_med, "ms_p10": ms_p10, "ms_p90": ms_p90,
-            "warm_ms": warm_ms, "wall_ms": wall_ms}
+            "warm_ms": warm_ms, "wall_ms": wall_ms, "graph_ms_med": float(np.median(gcold)),
+            "graph_warm_ms": graph_warm_ms}
 
 
 def density_of(s, d, n_sel, sel_count, sel_idx):
