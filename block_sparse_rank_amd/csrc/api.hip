@@ -73,7 +73,7 @@ int check_dims(const hsakv_dims* d) {
     if (d->Binter % 64 || d->Binter > 512 || d->Bintra % 64 || d->Bintra > 512)
         return HSAKV_ERR_UNSUPPORTED;
     if (d->r % 32 || d->r > 1024) return HSAKV_ERR_UNSUPPORTED;
-    if (d->Kp > 64 || d->H > kMaxHeads || (long long)d->H * d->d > 16384) return HSAKV_ERR_UNSUPPORTED;
+    if (d->Kp > kMaxKp || d->H > kMaxHeads || (long long)d->H * d->d > 16384) return HSAKV_ERR_UNSUPPORTED;
     const long long Tp = (long long)d->Psize * d->tokens_per_frame;
     if (Tp > (1LL << 30) || (long long)d->Kp * Tp + d->Lq >= (1LL << 31)) return HSAKV_ERR_BAD_DIMS;
     if (d->P > 65536) return HSAKV_ERR_UNSUPPORTED;
@@ -108,7 +108,7 @@ int done() {
 
 // ---- workspace sizes -------------------------------------------------------
 
-size_t ws_gather(const Geo& g) { return align_up((size_t)retrieve_slabs(g) * g.HD * 4); }
+size_t ws_gather(const Geo& g) { return align_up(retrieve_ws_bytes(g)); }
 
 size_t ws_select(const Geo& g) {
     return align_up((size_t)g.H * g.NQB * g.d * 4) + align_up((size_t)g.H * g.NB_max * g.d * 4) +
@@ -191,10 +191,10 @@ int check_tiers(const hsakv_tiers* t) {
 template <typename T>
 void run_gather(const Geo& g, const void* pool_k, const void* pool_v, const float* page_kmean,
                 const int32_t* page_prompt, int cur_prompt, const Policy& pol, const Tiers& tiers, const void* q,
-                int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist, float* partial, float* kb,
+                int32_t* page_idx, int32_t* n_sel, void* k_hist, void* v_hist, void* retrieve_ws, float* kb,
                 hipStream_t st) {
-    launch_q_partials<T>(g, q, partial, st);
-    launch_retrieve(g, partial, page_kmean, page_prompt, cur_prompt, pol.policy, pol.seed, page_idx, n_sel, st);
+    launch_retrieve<T>(g, q, page_kmean, page_prompt, cur_prompt, pol.policy, pol.seed, retrieve_ws, page_idx,
+                       n_sel, st);
     if (kb)   // the history blocks of the pooled keys come with the copy
         launch_gather_pool<T>(g, pool_k, pool_v, page_idx, n_sel, k_hist, v_hist, kb, tiers, st);
     else
@@ -368,11 +368,11 @@ HSAKV_API int hkv_gather(const hsakv_dims* dims, const void* pool_k, const void*
     if (dims->dtype == HSAKV_BF16)
         run_gather<bf16_t>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval),
                            tiers_of(tiers), q, page_idx,
-                           n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
+                           n_sel, k_hist, v_hist, ws, nullptr, st);
     else
         run_gather<float>(g, pool_k, pool_v, page_kmean, page_prompt, cur_prompt, policy_of(retrieval),
                           tiers_of(tiers), q, page_idx,
-                          n_sel, k_hist, v_hist, (float*)ws, nullptr, st);
+                          n_sel, k_hist, v_hist, ws, nullptr, st);
     return done();
 }
 
@@ -568,7 +568,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     const int eb = elt_bytes(dims);
     HSAKV_CHECK(check_ws(ws, ws_bytes, ws_forward(g, eb)));
     Carver c{(char*)ws, ws_bytes};
-    float* partial = (float*)c.take(ws_gather(g));
+    void* part = c.take(ws_gather(g));
     float* qb = (float*)c.take((size_t)g.H * g.NQB * g.d * 4);
     float* kb = (float*)c.take((size_t)g.H * g.NB_max * g.d * 4);
     float* zl = (float*)c.take((size_t)g.H * g.NQB * g.NB_max * 4);
@@ -594,7 +594,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
     hipStream_t st = (hipStream_t)stream;
     if (eb == 2) {
         run_gather<bf16_t>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol, tr,
-                           in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
+                           in->q, page_idx, n_sel, k_hist, v_hist, part, kb, st);
         // The low-rank branch needs the gathered KV only: with a fork it runs
         // on the caller's second stream beside the pooling, the block
         // selection and the sparse plan (small, latency-bound kernels), and
@@ -631,7 +631,7 @@ HSAKV_API int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_
                                    st);
     } else {
         run_gather<float>(g, in->pool_k, in->pool_v, in->page_kmean, in->page_prompt, cur_prompt, pol, tr,
-                          in->q, page_idx, n_sel, k_hist, v_hist, partial, kb, st);
+                          in->q, page_idx, n_sel, k_hist, v_hist, part, kb, st);
         run_select<float>(g, in->q, k_hist, in->k_intra, n_sel, t, sel_count, sel_idx, nullptr,
                           nullptr, qb, kb, zl, true, st);
         run_linear<float>(g, in->q, k_hist, v_hist, in->k_intra, in->v_intra, n_sel, in->E,

@@ -8,18 +8,156 @@
 #include "launch.h"
 
 // ---------------------------------------------------------------------------
-// Retrieval, step 1: partial column sums of q over token slabs (k_q_colsum,
-// below). The chunk mean is their sum in slab order, taken by step 2.
+// Rows of 8 elements as one 16-byte (bf16) or two (f32) vector loads.
 
-// Always 32 slabs (slabs past the chunk hold zero sums), so the chunk-mean
-// kernel loads every partial unconditionally.
-constexpr int kSlabs = 32;
-int retrieve_slabs(const Geo&) { return kSlabs; }
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+template <typename T> struct Row8;
+template <> struct Row8<bf16_t> {
+    u32x4 a;
+    HSAKV_DEV void load(const bf16_t* p) { a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+    HSAKV_DEV void store(bf16_t* p) const { *reinterpret_cast<u32x4*>(p) = a; }
+    HSAKV_DEV void add_to(float* acc) const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(w[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Row8<float> {
+    u32x4 a, b;
+    HSAKV_DEV void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
+    }
+    HSAKV_DEV void store(float* p) const {
+        reinterpret_cast<u32x4*>(p)[0] = a;
+        reinterpret_cast<u32x4*>(p)[1] = b;
+    }
+    HSAKV_DEV void add_to(float* acc) const {
+        acc[0] += __uint_as_float(a.x); acc[1] += __uint_as_float(a.y);
+        acc[2] += __uint_as_float(a.z); acc[3] += __uint_as_float(a.w);
+        acc[4] += __uint_as_float(b.x); acc[5] += __uint_as_float(b.y);
+        acc[6] += __uint_as_float(b.z); acc[7] += __uint_as_float(b.w);
+    }
+};
 
 // ---------------------------------------------------------------------------
-// Retrieval, step 2 (one block of 1024 threads): the chunk-mean query (slab
-// partials added in slab order, one column per thread), page scores, prompt
-// filter, top-Kp with ties to the lower page, slots ascending.
+// Retrieval, step 1 (k_slab_scores): the chunk's query sums and the terms of
+// the page scores. Work-group (slab s, 256 columns g) sums those columns of q
+// over the slab's rows in float64, writes the sums (colsum[s][c], kept for
+// step 2's exact path) and, for every page, the float64 dot product of the
+// sums with the page-mean key over the 256 columns: part[p][s G + g]. A page's
+// parts add up to Lq <page-mean key, chunk-mean query>, all H d columns.
+
+constexpr int kSlabs = 32;            // row slabs of q (and of a page, for the page means)
+constexpr int kQsumGroups = 16;       // row groups per work-group
+
+int retrieve_parts(const Geo& g) { return kSlabs * ((g.HD + 255) / 256); }
+
+// Rows r0 + grp, r0 + grp + 16, ... of the slab in order per thread (16 rows
+// in flight for bf16, 8 for f32), the 16 row groups added in group order.
+// The page terms: thread (page t / 16 of a pass of 32 pages, chunk t % 16)
+// takes the 16 columns of its chunk in order, and a page's 16 chunk sums are
+// added in chunk order.
+constexpr int kChunks = 16;                                  // 16-column chunks of the 256 columns
+constexpr int kPagesPerPass = 32 * kQsumGroups / kChunks;    // 32
+
+template <typename T>
+__global__ void __launch_bounds__(32 * kQsumGroups)
+k_slab_scores(const T* __restrict__ q, int Lq, int HD, int P, const float* __restrict__ page_kmean,
+              double* __restrict__ colsum, double* __restrict__ part) {
+    const int tid = threadIdx.x, lane = tid & 31, grp = tid >> 5;
+    const int slab = blockIdx.x, cg = blockIdx.y, G = gridDim.y;
+    const int col0 = (cg * 32 + lane) * 8;
+    const int ncol = HD - cg * 256 < 256 ? HD - cg * 256 : 256;   // a multiple of 64 (H d is one of 64)
+    const int pp = tid / kChunks, ch = tid % kChunks;
+    const bool ch_ok = kChunks * ch < ncol;
+    // the first pass's page means do not depend on q: loaded first (addresses
+    // clamped into the array, values of absent pages or chunks unused)
+    auto load_means = [&](int p, float4 (&kf)[4]) __attribute__((always_inline)) {
+        const int pc = p < P ? p : P - 1;
+        const float4* src =
+            reinterpret_cast<const float4*>(page_kmean + (size_t)pc * HD + cg * 256 + (ch_ok ? kChunks * ch : 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = src[i];
+    };
+    float4 kf[4];
+    load_means(pp, kf);
+    const int per = (Lq + kSlabs - 1) / kSlabs;
+    const int r0 = slab * per, r1 = r0 + per < Lq ? r0 + per : Lq;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (col0 < HD) {
+        constexpr int kRows = sizeof(T) == 2 ? 16 : 8;
+        for (int t = r0 + grp; t < r1; t += kQsumGroups * kRows) {
+            Row8<T> v[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                if (t + kQsumGroups * u < r1) v[u].load(q + (size_t)(t + kQsumGroups * u) * HD + col0);
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                if (t + kQsumGroups * u < r1) {
+                    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    v[u].add_to(x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += (double)x[e];
+                }
+        }
+    }
+    __shared__ double gs[kQsumGroups][256];
+    __shared__ double cs[256];
+    __shared__ double pd[kPagesPerPass][kChunks + 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gs[grp][lane * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < ncol) {
+        double a = 0.0;
+#pragma unroll
+        for (int g2 = 0; g2 < kQsumGroups; ++g2) a += gs[g2][tid];
+        cs[tid] = a;
+        colsum[(size_t)slab * HD + cg * 256 + tid] = a;
+    }
+    __syncthreads();
+    for (int p0 = 0; p0 < P; p0 += kPagesPerPass) {
+        if (p0 > 0) load_means(p0 + pp, kf);
+        double d = 0.0;
+        if (ch_ok) {
+            const double* c = cs + kChunks * ch;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                d = fma((double)kf[i].x, c[4 * i], d);
+                d = fma((double)kf[i].y, c[4 * i + 1], d);
+                d = fma((double)kf[i].z, c[4 * i + 2], d);
+                d = fma((double)kf[i].w, c[4 * i + 3], d);
+            }
+        }
+        pd[pp][ch] = d;
+        __syncthreads();
+        if (tid < kPagesPerPass && p0 + tid < P) {
+            double a = 0.0;
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) a += pd[tid][c];
+            part[(size_t)(p0 + tid) * G * kSlabs + slab * G + cg] = a;
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T>
+void launch_slab_scores(const Geo& g, const void* q, const float* page_kmean, double* colsum, double* part,
+                        hipStream_t st) {
+    const dim3 grid(kSlabs, (g.HD + 255) / 256);
+    hipLaunchKernelGGL(k_slab_scores<T>, grid, dim3(32 * kQsumGroups), 0, st, (const T*)q, g.Lq, g.HD, g.P,
+                       page_kmean, colsum, part);
+}
+template void launch_slab_scores<float>(const Geo&, const void*, const float*, double*, double*, hipStream_t);
+template void launch_slab_scores<bf16_t>(const Geo&, const void*, const float*, double*, double*, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Retrieval, step 2: scores, prompt filter, top-Kp with ties to the lower
+// page, slots in ascending page order.
 
 constexpr int kRetrieveThreads = 1024;
 
@@ -42,159 +180,171 @@ HSAKV_DEV bool policy_candidate(int policy, int prompt, int cur) {
         default: return true;                   // page-only, recent, random
     }
 }
+HSAKV_DEV bool policy_by_score(int policy) { return policy == 0 || policy == 1 || policy == 5; }
+
+// Step 2, one work-group (k_retrieve):
+// - a page's score is its parts added in float64 (segments of kSegParts
+//   parts in order, then the segments in order), divided by Lq and rounded
+//   to float32, the precision the ranking is decided in. A sum that is not
+//   finite means a NaN or an infinity among the page mean or the queries;
+//   such a page's score is then taken from the terms kbar[c] qbar[c] of the
+//   exact dot product (qbar from the slab sums), whose value is then +inf,
+//   -inf or NaN whatever the order of the sum. A score that is not a number
+//   ranks below every number, as -inf;
+// - the other policies' keys (page index, or SplitMix64 output p >> 40) are
+//   exact in float32;
+// - a candidate's rank counts the candidates with a better key, or an equal
+//   key and a lower index; the Kp best are chosen, and a chosen page's slot
+//   is the number of chosen pages below it.
+constexpr int kSegParts = 8;
 
 __global__ void __launch_bounds__(kRetrieveThreads)
-k_retrieve(const float* __restrict__ partial, int slabs, float inv_Lq, int HD, int P, int Kp,
-           const float* __restrict__ page_kmean, const int32_t* __restrict__ page_prompt,
-           int cur_prompt, int policy, unsigned long long seed, int32_t* __restrict__ page_idx,
-           int32_t* __restrict__ n_sel) {
-    extern __shared__ float smem[];
-    float* qbar = smem;                       // [HD]
-    float* score = smem + HD;                 // [P]
-    int* cand = reinterpret_cast<int*>(score + P);      // [P] 1 if the page matches
-    __shared__ int n_cand;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int nwaves = kRetrieveThreads / 64;
-
-    // columns tid and tid + 1024: both columns' slab partials in flight at once
-    (void)slabs;
-    for (int c = tid; c < HD; c += 2 * kRetrieveThreads) {
-        const int c2 = c + kRetrieveThreads < HD ? c + kRetrieveThreads : c;
-        float v[kSlabs], w[kSlabs];
+k_retrieve(const double* __restrict__ part, const double* __restrict__ colsum, const float* __restrict__ page_kmean,
+           int HD, int Lq, int P, int Kp, const int32_t* __restrict__ page_prompt, int cur_prompt, int policy,
+           unsigned long long seed, int32_t* __restrict__ page_idx, int32_t* __restrict__ n_sel) {
+    constexpr int NT = kRetrieveThreads, NWV = NT / 64;
+    extern __shared__ float smem[];   // key[P], cand[P]
+    float* key = smem;
+    int* cand = reinterpret_cast<int*>(smem + P);
+    __shared__ double seg[NT];
+    __shared__ double psum[NT];
+    __shared__ int wave_cnt[2 * NWV];
+    __shared__ int slot_page[kMaxKp];
+    __shared__ int flags;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool by_score = policy_by_score(policy);
+    // thread t adds segment t % nseg of page p0 + t / nseg (NG is a multiple
+    // of 32, so segments are whole); the first chunk's loads go out first
+    const int NG = kSlabs * ((HD + 255) / 256);
+    const int nseg = NG / kSegParts;   // at most 256
+    const int ppc = NT / nseg;
+    auto load_seg = [&](int p0, double (&v)[kSegParts]) __attribute__((always_inline)) {
+        const int p = p0 + tid / nseg;
+        const bool ok = tid < ppc * nseg && p < P;   // else a valid address, value unused
+        const double* src = part + (size_t)(ok ? p : 0) * NG + (ok ? tid % nseg : 0) * kSegParts;
 #pragma unroll
-        for (int k = 0; k < kSlabs; ++k) {
-            v[k] = partial[(size_t)k * HD + c];
-            w[k] = partial[(size_t)k * HD + c2];
-        }
-        float sv = 0.f, sw = 0.f;
-#pragma unroll
-        for (int k = 0; k < kSlabs; ++k) {
-            sv += v[k];
-            sw += w[k];
-        }
-        qbar[c] = sv * inv_Lq;
-        if (c + kRetrieveThreads < HD) qbar[c2] = sw * inv_Lq;
+        for (int i = 0; i < kSegParts; ++i) v[i] = src[i];
+    };
+    double v[kSegParts];
+    if (by_score) load_seg(0, v);
+    for (int p = tid; p < P; p += NT) {
+        const bool m = policy_candidate(policy, page_prompt[p], cur_prompt);
+        cand[p] = m ? 1 : 0;
+        if (!by_score) key[p] = m ? (policy == 4 ? (float)(splitmix64_at(seed, p) >> 40) : (float)p) : 0.f;
     }
-    if (tid == 0) n_cand = 0;
-    __syncthreads();
-
-    // page scores, one wave per page; lanes take columns lane, lane + 64, ...
-    // in a fixed order, then a fixed tree. A wave holds two pages at a time
-    // (pages w and w + 16), with both pages' loads in flight together.
-    const bool by_score = policy == 0 || policy == 1 || policy == 5;
-    for (int p0 = wave; p0 < P; p0 += 2 * nwaves) {
-        const int p1 = p0 + nwaves;
-        const bool m0 = policy_candidate(policy, page_prompt[p0], cur_prompt);
-        const bool m1 = p1 < P && policy_candidate(policy, page_prompt[p1], cur_prompt);
-        if (!by_score) {
-            // recency (the page index) or the random key: exact in float32
-            if (lane == 0) {
-                const float k0 = policy == 4 ? (float)(splitmix64_at(seed, p0) >> 40) : (float)p0;
-                score[p0] = m0 ? k0 : 0.f;
-                cand[p0] = m0 ? 1 : 0;
-                if (m0) atomicAdd(&n_cand, 1);
-                if (p1 < P) {
-                    const float k1 = policy == 4 ? (float)(splitmix64_at(seed, p1) >> 40) : (float)p1;
-                    score[p1] = m1 ? k1 : 0.f;
-                    cand[p1] = m1 ? 1 : 0;
-                    if (m1) atomicAdd(&n_cand, 1);
+    if (by_score) {
+        for (int p0 = 0; p0 < P; p0 += ppc) {
+            if (p0 > 0) load_seg(p0, v);
+            if (tid < ppc * nseg && p0 + tid / nseg < P) {
+                double a = 0.0;
+#pragma unroll
+                for (int i = 0; i < kSegParts; ++i) a += v[i];
+                seg[tid] = a;
+            }
+            __syncthreads();
+            bool bad = false;
+            if (tid < ppc && p0 + tid < P) {
+                double a = 0.0;
+#pragma unroll 8
+                for (int s2 = 0; s2 < nseg; ++s2) a += seg[tid * nseg + s2];
+                const float f = (float)(a / (double)Lq);
+                key[p0 + tid] = __builtin_isnan(f) ? -INFINITY : f;
+                psum[tid] = a;
+                bad = !__builtin_isfinite(a);
+            }
+            if (!__syncthreads_or(bad)) continue;
+            // the pages of this chunk whose sum is not finite, one at a time by the work-group
+            for (int i = 0; i < ppc && p0 + i < P; ++i) {
+                if (__builtin_isfinite(psum[i])) continue;   // uniform: every thread reads the same word
+                const int pg = p0 + i;
+                if (tid == 0) flags = 0;
+                __syncthreads();
+                int f = 0;   // bit 0: a NaN term, bit 1: +inf, bit 2: -inf
+                for (int c = tid; c < HD; c += NT) {
+                    double qs = 0.0;
+                    for (int sl = 0; sl < kSlabs; ++sl) qs += colsum[(size_t)sl * HD + c];
+                    const double t = (double)page_kmean[(size_t)pg * HD + c] * (qs / (double)Lq);
+                    f |= __builtin_isnan(t) ? 1 : __builtin_isinf(t) ? (t > 0 ? 2 : 4) : 0;
                 }
-            }
-            continue;
-        }
-        float s0 = 0.f, s1 = 0.f;
-        int c = lane;
-        const float* k0 = page_kmean + (size_t)p0 * HD;
-        const float* k1 = page_kmean + (size_t)(p1 < P ? p1 : p0) * HD;
-        // every page is loaded (a page past P reloads p0); only matching
-        // pages' scores are kept
-        for (; c + 23 * 64 < HD; c += 24 * 64) {
-            float a[24], b[24];
-#pragma unroll
-            for (int u = 0; u < 24; ++u) {
-                a[u] = k0[c + 64 * u];
-                b[u] = k1[c + 64 * u];
-            }
-#pragma unroll
-            for (int u = 0; u < 24; ++u) {
-                s0 = fmaf(a[u], qbar[c + 64 * u], s0);
-                s1 = fmaf(b[u], qbar[c + 64 * u], s1);
+                if (f) atomicOr(&flags, f);
+                __syncthreads();
+                if (tid == 0) {
+                    const int fl = flags;
+                    key[pg] = (fl & 1) || (fl & 6) == 6 ? -INFINITY : (fl & 2) ? INFINITY : -INFINITY;
+                }
+                __syncthreads();
             }
         }
-        for (; c < HD; c += 64) {
-            s0 = fmaf(k0[c], qbar[c], s0);
-            s1 = fmaf(k1[c], qbar[c], s1);
+    } else {
+        __syncthreads();
+    }
+    // rank and slot: each thread compares its page with every other, eight at
+    // a time (no early exit, so a group's LDS reads are in flight together);
+    // the slot is the ballot prefix within the pass plus the passes before
+    int carry = 0, ncand = 0;
+    for (int base = 0; base < P; base += NT) {
+        const int p = base + tid;
+        const bool is_c = p < P && cand[p] != 0;
+        bool pick = false;
+        if (is_c) {
+            const float kp = key[p];
+            int rank = 0;
+#pragma unroll 8
+            for (int o = 0; o < P; ++o) {
+                const float ko = key[o];
+                rank += (cand[o] != 0 && (ko > kp || (ko == kp && o < p))) ? 1 : 0;
+            }
+            pick = rank < Kp;
         }
-        s0 = wave_sum(s0);
-        s1 = wave_sum(s1);
-        // a score that is not a number ranks below every number: with -inf
-        // the rank test below is a total order (ties to the lower page), so
-        // exactly min(Kp, candidates) pages are chosen
-        if (__builtin_isnan(s0)) s0 = -INFINITY;
-        if (__builtin_isnan(s1)) s1 = -INFINITY;
+        const unsigned long long bp = __builtin_amdgcn_ballot_w64(pick);
+        const unsigned long long bc = __builtin_amdgcn_ballot_w64(is_c);
         if (lane == 0) {
-            score[p0] = m0 ? s0 : 0.f;
-            cand[p0] = m0 ? 1 : 0;
-            if (m0) atomicAdd(&n_cand, 1);
-            if (p1 < P) {
-                score[p1] = m1 ? s1 : 0.f;
-                cand[p1] = m1 ? 1 : 0;
-                if (m1) atomicAdd(&n_cand, 1);
-            }
+            wave_cnt[2 * wave] = __builtin_popcountll(bp);
+            wave_cnt[2 * wave + 1] = __builtin_popcountll(bc);
         }
-    }
-    __syncthreads();
-
-    // rank of each candidate: better score, or equal score and lower index;
-    // the Kp best are marked chosen (cand = 2; still nonzero for the others'
-    // candidate test)
-    for (int p = tid; p < P; p += kRetrieveThreads) {
-        if (!cand[p]) continue;
-        const float sp = score[p];
-        int rank = 0;
-        for (int o = 0; o < P && rank < Kp; ++o) {
-            if (!cand[o] || o == p) continue;
-            const float so = score[o];
-            if (so > sp || (so == sp && o < p)) ++rank;
+        __syncthreads();
+        int below = 0, tp = 0, tc = 0;
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) {
+            below += v < wave ? wave_cnt[2 * v] : 0;
+            tp += wave_cnt[2 * v];
+            tc += wave_cnt[2 * v + 1];
         }
-        if (rank < Kp) cand[p] = 2;
+        if (pick) slot_page[carry + below + __builtin_popcountll(bp & ((1ull << lane) - 1ull))] = p;
+        carry += tp;
+        ncand += tc;
+        __syncthreads();   // wave_cnt is rewritten by the next pass; slot_page is complete after the last
     }
-    __syncthreads();
-
-    // slots in ascending page order: a chosen page's slot is the number of
-    // chosen pages below it
-    const int n = n_cand < Kp ? n_cand : Kp;
-    for (int p = tid; p < P; p += kRetrieveThreads) {
-        if (cand[p] != 2) continue;
-        int slot = 0;
-        for (int o = 0; o < p; ++o) slot += cand[o] == 2 ? 1 : 0;
-        page_idx[slot] = p;
-    }
-    for (int k = n + tid; k < Kp; k += kRetrieveThreads) page_idx[k] = -1;
+    const int n = ncand < Kp ? ncand : Kp;
+    for (int k = tid; k < Kp; k += NT) page_idx[k] = k < n ? slot_page[k] : -1;
     if (tid == 0) *n_sel = n;
 }
 
-size_t retrieve_smem_bytes(const Geo& g) {
-    return (size_t)g.HD * 4 + (size_t)g.P * 8;
-}
+size_t retrieve_smem_bytes(const Geo& g) { return (size_t)g.P * 8; }
 
-void launch_retrieve(const Geo& g, const float* partial, const float* page_kmean,
-                     const int32_t* page_prompt, int cur_prompt, int policy, unsigned long long seed,
-                     int32_t* page_idx, int32_t* n_sel, hipStream_t st) {
-    hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st, partial,
-                       retrieve_slabs(g), 1.0f / (float)g.Lq, g.HD, g.P, g.Kp, page_kmean, page_prompt,
-                       cur_prompt, policy, seed, page_idx, n_sel);
+// part[P][retrieve_parts] then, 256-byte aligned, colsum[kSlabs][HD], both float64
+size_t retrieve_part_bytes(const Geo& g) { return ((size_t)g.P * retrieve_parts(g) * 8 + 255) / 256 * 256; }
+size_t retrieve_ws_bytes(const Geo& g) { return retrieve_part_bytes(g) + (size_t)kSlabs * g.HD * 8; }
+
+template <typename T>
+void launch_retrieve(const Geo& g, const void* q, const float* page_kmean, const int32_t* page_prompt,
+                     int cur_prompt, int policy, unsigned long long seed, void* ws, int32_t* page_idx,
+                     int32_t* n_sel, hipStream_t st) {
+    double* part = (double*)ws;
+    double* colsum = (double*)((char*)ws + retrieve_part_bytes(g));
+    if (policy == 0 || policy == 1 || policy == 5) launch_slab_scores<T>(g, q, page_kmean, colsum, part, st);
+    hipLaunchKernelGGL(k_retrieve, dim3(1), dim3(kRetrieveThreads), retrieve_smem_bytes(g), st, part, colsum,
+                       page_kmean, g.HD, g.Lq, g.P, g.Kp, page_prompt, cur_prompt, policy, seed, page_idx, n_sel);
 }
+template void launch_retrieve<float>(const Geo&, const void*, const float*, const int32_t*, int, int,
+                                     unsigned long long, void*, int32_t*, int32_t*, hipStream_t);
+template void launch_retrieve<bf16_t>(const Geo&, const void*, const float*, const int32_t*, int, int,
+                                      unsigned long long, void*, int32_t*, int32_t*, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Gather: slot s of the active cache <- pool page page_idx[s], for K and V.
 // A pure HBM-to-HBM copy: 16-byte vectors, kGatherUnroll loads in flight per
 // thread before the stores. blockIdx.y = slot, blockIdx.z = 0 for K, 1 for V.
-
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 8;
@@ -244,38 +394,6 @@ k_gather(const u32x4* __restrict__ pool_k, const u32x4* __restrict__ pool_v,
 // grp, grp + 8, ... of the block in row order, and the eight row groups are
 // added in group order: the same float32 operations as the pooling of a
 // gathered block, so both give the same pooled key.
-
-template <typename T> struct Row8;
-template <> struct Row8<bf16_t> {
-    u32x4 a;
-    HSAKV_DEV void load(const bf16_t* p) { a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
-    HSAKV_DEV void store(bf16_t* p) const { *reinterpret_cast<u32x4*>(p) = a; }
-    HSAKV_DEV void add_to(float* acc) const {
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += __uint_as_float(w[i] << 16);
-            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
-        }
-    }
-};
-template <> struct Row8<float> {
-    u32x4 a, b;
-    HSAKV_DEV void load(const float* p) {
-        a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-        b = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 4));
-    }
-    HSAKV_DEV void store(float* p) const {
-        reinterpret_cast<u32x4*>(p)[0] = a;
-        reinterpret_cast<u32x4*>(p)[1] = b;
-    }
-    HSAKV_DEV void add_to(float* acc) const {
-        acc[0] += __uint_as_float(a.x); acc[1] += __uint_as_float(a.y);
-        acc[2] += __uint_as_float(a.z); acc[3] += __uint_as_float(a.w);
-        acc[4] += __uint_as_float(b.x); acc[5] += __uint_as_float(b.y);
-        acc[6] += __uint_as_float(b.z); acc[7] += __uint_as_float(b.w);
-    }
-};
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -393,7 +511,6 @@ void launch_gather(const Geo& g, int elt_bytes, const void* pool_k, const void* 
 // lanes of 8 elements x 16 row groups, 16 rows (bf16; 8 for f32) in flight
 // per thread. Each thread keeps a Kahan sum per column over its rows in row
 // order; the 16 group sums are added in group order (Kahan).
-constexpr int kQsumGroups = 16;
 
 template <typename T>
 __global__ void __launch_bounds__(32 * kQsumGroups)
@@ -471,15 +588,6 @@ void launch_page_summary(const Geo& g, const void* pool_k, float* page_kmean, fl
 template void launch_page_summary<float>(const Geo&, const void*, float*, float*, hipStream_t);
 template void launch_page_summary<bf16_t>(const Geo&, const void*, float*, float*, hipStream_t);
 
-// Slab column sums of q for the chunk mean: q is one item of Lq rows.
-template <typename T>
-void launch_q_partials(const Geo& g, const void* q, float* partial, hipStream_t st) {
-    dim3 grid(kSlabs, (g.HD + 255) / 256);
-    hipLaunchKernelGGL(k_slab_colsum<T>, grid, dim3(32 * kQsumGroups), 0, st, (const T*)q, (long long)g.Lq, g.HD,
-                       partial);
-}
-template void launch_q_partials<float>(const Geo&, const void*, float*, hipStream_t);
-template void launch_q_partials<bf16_t>(const Geo&, const void*, float*, hipStream_t);
 
 // ---------------------------------------------------------------------------
 // Page commit: the chunk's K and V rows become history tokens [fill, fill + n)

@@ -32,12 +32,15 @@ template <typename T>
 void launch_page_commit(const Geo&, void* pool_k, void* pool_v, float* page_kmean, int32_t* page_prompt,
                         const void* k_chunk, const void* v_chunk, int n, long long fill, int cur_prompt,
                         float* partial, hipStream_t);
-int retrieve_slabs(const Geo&);
+constexpr int kMaxKp = 64;   // active-cache slots at most
+
+// Retrieval (two kernels; the first for the score policies only): the
+// workspace holds retrieve_ws_bytes bytes of float64 partial sums.
 size_t retrieve_smem_bytes(const Geo&);
-template <typename T> void launch_q_partials(const Geo&, const void* q, float* partial, hipStream_t);
-void launch_retrieve(const Geo&, const float* partial, const float* page_kmean, const int32_t* page_prompt,
-                     int cur_prompt, int policy, unsigned long long seed, int32_t* page_idx, int32_t* n_sel,
-                     hipStream_t);
+size_t retrieve_ws_bytes(const Geo&);
+template <typename T>
+void launch_retrieve(const Geo&, const void* q, const float* page_kmean, const int32_t* page_prompt, int cur_prompt,
+                     int policy, unsigned long long seed, void* ws, int32_t* page_idx, int32_t* n_sel, hipStream_t);
 void launch_gather(const Geo&, int elt_bytes, const void* pool_k, const void* pool_v, const int32_t* page_idx,
                    const int32_t* n_sel, void* k_hist, void* v_hist, const Tiers& tiers, hipStream_t);
 // The gather with the history blocks of the pooled keys kb written on the way.

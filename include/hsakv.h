@@ -270,7 +270,9 @@ int hkv_page_commit(const hsakv_dims* dims, void* pool_k, void* pool_v, float* p
  *  1. Prompt stage: candidates are the pages with page_prompt[p] == cur_prompt
  *     (the single matching prompt: Top-1, per the open-questions paragraph).
  *  2. Page stage: s_p = sum over heads and dims of page_kmean[p] * mean-over-
- *     chunk(q), in float32. The min(Kp, #candidates) best pages are kept,
+ *     chunk(q), summed in float64 and rounded to float32, the precision the
+ *     ranking is decided in (a score that is not a number ranks below every
+ *     number). The min(Kp, #candidates) best pages are kept,
  *     equal scores to the lower page index, and stored in ascending page
  *     order: page_idx[0..n_sel) (device, int32 [Kp]; entries past n_sel are
  *     set to -1) and *n_sel (device).

@@ -391,6 +391,27 @@ def test_retrieval_policies(policy, Kp, seed):
     assert host(k_hist)[:n * s.Tp].tobytes() == np.concatenate([c.pool_k[p] for p in want]).tobytes()
 
 
+@pytest.mark.parametrize("policy", ["two_stage", "page_only", "recent", "random"])
+def test_retrieval_over_more_pages_than_threads(policy):
+    """1100 pages, more than the 1024 pages one ranking pass covers, and Kp =
+    64: the chosen pages lie on both sides of the pass boundary (the recency
+    policy takes the newest candidates, all above it) and their slots, in
+    ascending page order, equal the oracle's."""
+    P, Kp = 1100, 64
+    s = synth.shape("tiny").with_(P=P, Kp=Kp, tokens_per_frame=1, Psize=8, seed=36)
+    prompts = np.array([p % 2 for p in range(P)], np.int32)
+    c = Case(s, page_prompt=prompts, cur_prompt=0)
+    km = c.page_summary()
+    kmh = host(km).astype(np.float64)
+    qbar = oracle.chunk_query_mean(oracle.as_f64(c.ch["q"], s.dtype))
+    want, n = oracle.retrieve(kmh, prompts, 0, qbar, Kp, policy, 5)
+    assert n == Kp and want.max() >= 1024 and (policy == "recent" or want.min() < 1024)
+    page_idx, n_sel, k_hist, _ = c.gather(km, policy=policy, seed=5)
+    assert int(host(n_sel)[0]) == n
+    assert host(page_idx).tolist() == want.tolist(), (policy, host(page_idx), want)
+    assert host(k_hist).tobytes() == np.concatenate([c.pool_k[p] for p in want]).tobytes()
+
+
 @pytest.mark.parametrize("policy", ["recent", "random", "mismatched"])
 def test_forward_with_other_policies(policy):
     s = synth.shape("tiny").with_(dtype="bf16", P=10, Kp=3, clustered=True, tau_law="uniform", seed=35)
