@@ -251,38 +251,39 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 // ---- 256 x 256 tiles ---------------------------------------------------------
 //
 // For r >= 128 and H*d a multiple of 256 the output tile is 256 (m) x 256 (n)
-// with 32-wide k-steps: a k-step reads E's slice once per 256 columns of
-// keys and each key slice once per 256 rows of E (half and a quarter of the
-// L2 reads of 128 x 128 tiles), 8 waves (wave w: rows 128 (w % 2), columns
-// 64 (w / 2), eight 32x32 accumulators), one work-group per CU and a ring of
-// four LDS stages, three in flight, so the stream keeps enough bytes in
-// flight. The 16-byte chunks of a row are XOR-swizzled in LDS for
-// conflict-free operand reads, with rows unpadded so every DMA lane loads
-// data and each row's bytes stay contiguous: X (64-byte rows) slot s of row r
-// holds chunk s ^ (r / 4 mod 4), so the 16 rows of one b128 read phase fall
-// on distinct banks; Y (512-byte rows) slot s of row r holds chunk
-// s ^ 4 (r mod 4), so the 4 rows x 4 chunks of a transpose read's 32 lanes do.
+// with 64-wide k-steps: a k-step reads E's slice once per 256 columns of keys
+// and each key slice once per 256 rows of E (half and a quarter of the L2
+// reads of 128 x 128 tiles), and each of the 256 E rows of a step is one
+// whole 128-byte line. 8 waves (wave w: rows 128 (w % 2), columns 64 (w / 2),
+// eight 32x32 accumulators), one work-group per CU and two 64 KB LDS stages,
+// the next step's DMA in flight during a step's MFMA work. The 16-byte chunks
+// of a row are XOR-swizzled in LDS for conflict-free operand reads, with rows
+// unpadded so every DMA lane loads data and each row's bytes stay contiguous:
+// X (128-byte rows) slot s of row r holds chunk s ^ (r / 2 mod 8), so the 16
+// rows of one b128 read phase fall on distinct banks; Y (512-byte rows) slot s
+// of row r holds chunk s ^ 4 (r mod 4), so the 4 rows x 4 chunks of a
+// transpose read's 32 lanes do.
 //
 // The k-steps of a split run over its history part, then its chunk part, each
 // ending in a partial step, so no step straddles the seam. The DMA goes
 // through buffer loads whose resource covers exactly the valid bytes: a Y row
 // past the part's end, or an X column past the end of E, is out of range and
 // not read; its LDS row is zeroed before use.
-constexpr int WM = 256, WN = 256, WK = 32, WT = 512, WWV = 8, WSTAGES = 4;
-constexpr int WA_SLOTS = WK / 8;               // 4 chunks per X row
+constexpr int WM = 256, WN = 256, WK = 64, WT = 512, WWV = 8, WSTAGES = 2;
+constexpr int WA_SLOTS = WK / 8;               // 8 chunks per X row
 constexpr int WB_SLOTS = WN / 8;               // 32 chunks per Y row
-constexpr int WA_ROWB = WA_SLOTS * 16;         // 64
+constexpr int WA_ROWB = WA_SLOTS * 16;         // 128
 constexpr int WB_ROWB = WB_SLOTS * 16;         // 512
-constexpr int WA_BYTES = WM * WA_ROWB;         // 16384
-constexpr int WB_BYTES = WK * WB_ROWB;         // 16384
-constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 32768; four stages 131072 bytes
-constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 16
-constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 16
-constexpr int W_PER = 4;                       // DMA instructions per wave and k-step
+constexpr int WA_BYTES = WM * WA_ROWB;         // 32768
+constexpr int WB_BYTES = WK * WB_ROWB;         // 32768
+constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 65536; two stages 131072 bytes
+constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 32
+constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 32
+constexpr int W_PER = 8;                       // DMA instructions per wave and k-step
 static_assert(WM * WA_SLOTS % 64 == 0 && WK * WB_SLOTS % 64 == 0, "whole wave instructions");
 static_assert(WA_BYTES == WA_INSTR * 1024, "Y follows X in instruction order");
 static_assert(WA_INSTR + WB_INSTR == WWV * W_PER, "every wave sends the same count");
-HSAKV_DEV int xswz(int row) { return (row >> 2) & 3; }   // X chunk swizzle
+HSAKV_DEV int xswz(int row) { return (row >> 1) & 7; }   // X chunk swizzle
 HSAKV_DEV int yswz(int row) { return 4 * (row & 3); }    // Y chunk swizzle
 
 // Raw buffer resource: base p, `bytes` in range, 32-bit untyped data.
@@ -300,18 +301,14 @@ HSAKV_DEV lds_void_t* w_dst(char* p) {
     return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
 }
 
-template <int N>
-HSAKV_DEV void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
-}
+HSAKV_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // LDS-only work-group barrier (DMA in flight stays in flight).
 HSAKV_DEV void w_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Byte offsets of this wave's DMA instructions j = wave + 8 q (fixed over
-// the k-steps): X (j < 16) m * L + 8 chunk from the step's first column,
-// Y (j >= 16) row * HD + n0 + 8 chunk from the step's first row, the chunk a
+// the k-steps): X (j < 32) m * L + 8 chunk from the step's first column,
+// Y (j >= 32) row * HD + n0 + 8 chunk from the step's first row, the chunk a
 // lane's LDS slot holds under the swizzle.
 HSAKV_DEV void w_lanes(uint32_t (&off)[W_PER], const Geo& g, int wave, int m0, int n0) {
     const int lane = threadIdx.x & 63;
@@ -337,24 +334,25 @@ HSAKV_DEV void w_zero_tail(char* buf, int first) {
 
 typedef __attribute__((ext_vector_type(2))) unsigned w_u32x2_t;
 
-// One k-step of MFMA work. The eight transpose reads of Y sit in one asm
-// block that waits for them itself: issued as builtins, they would make the
-// compiler wait for every DMA in flight first (the next steps included).
-HSAKV_DEV void w_compute(const char* buf, f32x16_t (&acc)[4][2], int wave) {
+// Keys 32 h .. 32 h + 31 of a k-step (two 16-wide MFMA steps). The eight
+// transpose reads of Y sit in one asm block that waits for them itself:
+// issued as builtins, they would make the compiler wait for every DMA in
+// flight first (the next step's included).
+HSAKV_DEV void w_compute(const char* buf, f32x16_t (&acc)[4][2], int wave, int h) {
     const int lane = threadIdx.x & 63;
     const int mw = wave & 1, nw = wave >> 1;
     const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
-    // X row 128 mw + 32 mt + r32 has swizzle xswz(r32); chunk 2 kk + g2 sits in slot (2 kk + g2) ^ xswz
+    // X row 128 mw + 32 mt + r32 has swizzle xswz(r32); chunk 4 h + 2 kk + g2 sits in slot chunk ^ xswz
     const char* Arow = buf + (128 * mw + r32) * WA_ROWB;
-    const char* A0 = Arow + 16 * (g2 ^ xswz(r32));
-    const char* A1 = Arow + 16 * ((2 + g2) ^ xswz(r32));
-    // Y rows 16 kk + 4 h + 8 (G / 2) + j / 4 have swizzle yswz(j / 4); the 8 columns of
+    const char* A0 = Arow + 16 * ((4 * h + g2) ^ xswz(r32));
+    const char* A1 = Arow + 16 * ((4 * h + 2 + g2) ^ xswz(r32));
+    // Y rows 32 h + 16 kk + 4 e + 8 (G / 2) + j / 4 have swizzle yswz(j / 4); the 8 columns of
     // chunk 8 nw + 4 nt + 2 (G & 1) + (j & 3) / 2 sit in slot chunk ^ yswz, at byte 8 (j & 1)
     const int cy = 8 * nw + 2 * (G & 1) + ((j & 3) >> 1);
-    const char* Brow = buf + WA_BYTES + (8 * (G >> 1) + (j >> 2)) * WB_ROWB + 8 * (j & 1);
+    const char* Brow = buf + WA_BYTES + (32 * h + 8 * (G >> 1) + (j >> 2)) * WB_ROWB + 8 * (j & 1);
     const uint32_t bb0 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * (cy ^ yswz(j >> 2)));
     const uint32_t bb1 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * ((cy + 4) ^ yswz(j >> 2)));
-    // r[4 kk + 2 nt + h]: k rows 16 kk + 4 h (+ 8 (G / 2) + j / 4), columns 32 nt + ...
+    // r[4 kk + 2 nt + e]: k rows 16 kk + 4 e (+ 8 (G / 2) + j / 4), columns 32 nt + ...
     constexpr int H = 4 * WB_ROWB, K1 = 16 * WB_ROWB;
     bf16x8_t a0[4], a1[4];
 #pragma unroll
@@ -430,8 +428,8 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
     w_lanes(off, g, wave, m0, n0);
     const long long xbytes = 2LL * g.r * g.L;
 
-    // Send k-step s into its ring stage: per instruction a uniform resource
-    // (X, Y or the empty one of the idle instructions) and LDS target.
+    // Send k-step s into its stage: per instruction a uniform resource (X or
+    // Y) and LDS target.
     auto send = [&](int s) __attribute__((always_inline)) {
         if (s >= n) return;
         const bool hist = s < nh;
@@ -442,7 +440,7 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
         const int rows = end - k < WK ? (int)(end - k) : WK;
         const __amdgpu_buffer_rsrc_t rx = w_rsrc(X + col, xbytes - 2 * col);
         const __amdgpu_buffer_rsrc_t ry = w_rsrc(yb, 2LL * rows * g.HD);
-        char* buf = ring + (s & 3) * WSTAGE;
+        char* buf = ring + (s & 1) * WSTAGE;
 #pragma unroll
         for (int q = 0; q < W_PER; ++q) {
             const int j = wave + WWV * q;
@@ -459,20 +457,13 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16_t{};
 
     send(0);
-    send(1);
-    send(2);
 #pragma unroll 1
     for (int i = 0; i < n; ++i) {
-        // step i has landed once only the steps sent after it are outstanding
-        const int later = (n < i + 3 ? n : i + 3) - i - 1;
-        if (later >= 2)
-            wait_vm<2 * W_PER>();
-        else if (later == 1)
-            wait_vm<W_PER>();
-        else
-            wait_vm<0>();
+        // step i is the only one in flight; the barrier also retires every
+        // wave's reads of the other stage (step i - 1), which step i + 1 refills
+        wait_vm0();
         w_barrier();
-        char* now = ring + (i & 3) * WSTAGE;
+        char* now = ring + (i & 1) * WSTAGE;
         const bool hist = i < nh;
         const long long k = hist ? kb + (long long)i * WK : cb + (long long)(i - nh) * WK;
         const long long end = hist ? he : ke;
@@ -480,8 +471,9 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
             w_zero_tail(now, (int)(end - k));
             w_barrier();
         }
-        send(i + 3);
-        w_compute(now, acc, wave);
+        send(i + 1);
+        w_compute(now, acc, wave, 0);
+        w_compute(now, acc, wave, 1);
     }
 
     const int lane = threadIdx.x & 63;
