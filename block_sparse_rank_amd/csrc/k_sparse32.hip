@@ -56,6 +56,7 @@ constexpr int kSparseMaxWg = 256; // attention work-groups at most (partials are
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -174,13 +175,15 @@ HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float 
         for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < t ? s[i] : -INFINITY;
     }
     // raw scores: the max is taken before scaling (scale > 0), and the scale
-    // folds into the exponent's FMA
+    // folds into the exponent's FMA. The NaN-propagating maximum maps to a
+    // chain of three-input max instructions with no operand quieting (a NaN
+    // score makes its row NaN either way, through its own weight)
     float mx = s[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[i]);
     // lanes l and l + 32 hold the two key quarters of the same query
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float mt = mx * scale_log2;
     const bool moved = mt > w.m + kLazyMax;
     const float m_new = moved ? mt : w.m;
@@ -210,18 +213,21 @@ HSAKV_DEV void pv_half(Wave<D>& w, const f32x16_t& s, const char* vt, int sub) {
     constexpr int DT = Wave<D>::DT;
     const int lane = threadIdx.x & 63;
     const int G = lane >> 4, j = lane & 15;
+    // the weights as bf16 pairs, one packed conversion each; the row sum is
+    // taken on the same pairs
+    bf16x2_t pp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pp[i] = __builtin_convertvector((f32x2_t){s[2 * i], s[2 * i + 1]}, bf16x2_t);
     bf16x8_t pf[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[c][e] = (__bf16)s[8 * c + e];
+        pf[c] = __builtin_shufflevector(__builtin_shufflevector(pp[4 * c], pp[4 * c + 1], 0, 1, 2, 3),
+                                        __builtin_shufflevector(pp[4 * c + 2], pp[4 * c + 3], 0, 1, 2, 3),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float rs = w.l;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[c][2 * e], pf[c][2 * e + 1]}, ones, rs, false);
+    for (int i = 0; i < 8; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, rs, false);
     w.l = rs;
     i16x4_t lo[2][DT], hi[2][DT];
 #pragma unroll
