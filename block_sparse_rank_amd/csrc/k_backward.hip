@@ -28,7 +28,7 @@
 //   k_bwd_lowrank     per (128 projected keys, head, query slice): partial
 //                     dK', dV' on MFMA, queries streamed through LDS
 //   k_bwd_lowrank_sum the slice partials in slice order -> dK', dV' hi + lo
-//   k_bwd_proj        dE, dF = dK' K^T, dV' V^T: 256 x 256 tiles, the
+//   k_bwd_proj        dE, dF = dK' K^T, dV' V^T: 256-row tiles of 448 columns, the
 //                     contraction over H d through a 3-stage LDS DMA ring
 #include "common.h"
 #include "launch.h"
@@ -428,7 +428,7 @@ k_bwd_lowrank_sum(long long n, int nslices, const float* __restrict__ pk, const 
 
 // ---- dE, dF --------------------------------------------------------------------
 
-constexpr int QM = 256, QN = 256, QK = 32;   // tile rows (of r), columns (of L), contraction step
+constexpr int QM = 256, QN = 256, QK = 32;   // tile rows (of r), key rows per step (columns of L), contraction step
 constexpr int Q_ROW = QK * 2;                // bytes per LDS row: 4 chunks of 16, XOR-swizzled
 constexpr int Q_AHI = 0, Q_ALO = QM * Q_ROW, Q_B = 2 * QM * Q_ROW;
 constexpr int Q_STAGE = 2 * QM * Q_ROW + QN * Q_ROW;   // 48 KiB: 48 DMA instructions of 1 KiB
@@ -467,47 +467,41 @@ HSAKV_DEV void q_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::
 
 // dE (z = 0) or dF (z = 1) = dK' K_act^T (dV' V_act^T), written at the E/F
 // columns of the active keys, zeros at the columns of absent slots.
-// Work-group = 8 waves over a 256 x 256 tile (wave w: rows 64 (w % 4),
-// columns 128 (w / 4), 2 x 4 MFMA tiles). A tile's columns lie either in the
-// history part [0, Kp Tp) or in the chunk part [Kp Tp, L), so its key rows
-// come from one array: a history tile starting at or past the present rows
-// n_sel Tp is all zero. The contraction over the H d columns of the key rows
-// runs in 32-column steps through a 3-stage LDS ring filled by buffer-to-LDS
-// DMA (dK' hi, dK' lo, key rows; rows past r or past the tile's present keys
-// read as zero, and their products are zero), two steps in flight. The hi and lo parts of dK' are two
-// products into one accumulator.
-__global__ void __launch_bounds__(512, 1)
-k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
-           const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
-           const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo, const bf16_t* __restrict__ vhi,
-           const bf16_t* __restrict__ vlo, float* __restrict__ dE, float* __restrict__ dF) {
-    __shared__ __attribute__((aligned(16))) char ring[Q_STAGES * Q_STAGE];
-    const int z = blockIdx.z;
+// Work-group = 8 waves over QR = 448 columns of one part (history [0, Kp Tp)
+// or chunk [Kp Tp, L)), taken as a 256-column chunk and then a 192-column
+// one, so that the 2 x ceil(L / 448) work-groups of the 1.3B and 14B shapes
+// run in a single round on 256 CUs (256-column tiles alone would need two,
+// the second two-thirds full). In a chunk of 32 NTN columns per wave (NTN = 4
+// or 3), wave w takes rows 64 (w % 4) and columns 32 NTN (w / 4), 2 x NTN MFMA
+// tiles. A history chunk starting at or past the present rows n_sel Tp is all
+// zero. The contraction over the H d columns of the key rows runs in
+// 32-column steps through a 3-stage LDS ring filled by buffer-to-LDS DMA
+// (dK' hi, dK' lo, 256 key rows; rows past r or past the chunk's present keys
+// read as zero, and their products are zero), two steps in flight. The hi and
+// lo parts of dK' are two products into one accumulator.
+constexpr int QR = 448;   // columns per work-group: a 256-column chunk, then a 192-column one
+
+template <int NTN>
+HSAKV_DEV void bwd_proj_chunk(const Geo& g, char* ring, int z, int m0, long long c0, long long c_end, long long Lh,
+                              bool hist, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+                              const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
+                              const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo,
+                              const bf16_t* __restrict__ vhi, const bf16_t* __restrict__ vlo,
+                              float* __restrict__ out) {
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g2 = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 3, wn = wave >> 2;
-    int ns = *n_sel_p;
-    ns = ns < 0 ? 0 : (ns > g.Kp ? g.Kp : ns);
-    const long long Lh = (long long)ns * g.Tp;
-    float* out = z ? dF : dE;
-    const int nht = (int)((g.hist_rows + QN - 1) / QN);
-    const bool hist_tile = (int)blockIdx.x < nht;
-    const long long c0 = hist_tile ? (long long)blockIdx.x * QN : g.hist_rows + (long long)(blockIdx.x - nht) * QN;
-    const long long c_end = hist_tile ? (c0 + QN < g.hist_rows ? c0 + QN : g.hist_rows) : (c0 + QN < g.L ? c0 + QN : g.L);
-    const int m0 = blockIdx.y * QM;
-
-    if (hist_tile && c0 >= Lh) {
-        for (int i = tid; i < QM * QN; i += 512) {
-            const int m = m0 + i / QN;
-            const long long c = c0 + i % QN;
+    constexpr int CW = 64 * NTN;   // chunk columns
+    if (hist && c0 >= Lh) {
+        for (int i = tid; i < QM * CW; i += 512) {
+            const int m = m0 + i / CW;
+            const long long c = c0 + i % CW;
             if (m < g.r && c < c_end) out[(long long)m * g.L + c] = 0.f;
         }
         return;
     }
-
-    const bf16_t* keys = hist_tile ? (z ? v_hist : k_hist) + c0 * g.HD
-                                   : (z ? v_intra : k_intra) + (c0 - g.hist_rows) * g.HD;
-    const long long key_rows = (hist_tile ? (Lh < c_end ? Lh : c_end) : c_end) - c0;
+    const bf16_t* keys = hist ? (z ? v_hist : k_hist) + c0 * g.HD : (z ? v_intra : k_intra) + (c0 - g.hist_rows) * g.HD;
+    const long long key_rows = (hist ? (Lh < c_end ? Lh : c_end) : c_end) - c0;
     const long long row_bytes = 2LL * g.HD;
     const __amdgpu_buffer_rsrc_t rb = q_rsrc(keys, key_rows * row_bytes);
     const __amdgpu_buffer_rsrc_t rh = q_rsrc((z ? vhi : khi) + (long long)m0 * g.HD, (g.r - m0) * row_bytes);
@@ -538,11 +532,11 @@ k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ 
         }
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][NTN];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x16_t{};
+        for (int nt = 0; nt < NTN; ++nt) acc[mt][nt] = f32x16_t{};
     send(0);
     send(1);
 #pragma unroll 1
@@ -558,7 +552,7 @@ k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ 
 #pragma unroll
         for (int ks = 0; ks < QK / 16; ++ks) {
             const int ch = 2 * ks + g2;
-            bf16x8_t ah[2], al[2], b[4];
+            bf16x8_t ah[2], al[2], b[NTN];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int row = 64 * wm + 32 * mt + l32;
@@ -566,23 +560,25 @@ k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ 
                 al[mt] = ld8(buf + Q_ALO + pslot(row, ch));
             }
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) b[nt] = ld8(buf + Q_B + pslot(128 * wn + 32 * nt + l32, ch));
+            for (int nt = 0; nt < NTN; ++nt) b[nt] = ld8(buf + Q_B + pslot(32 * NTN * wn + 32 * nt + l32, ch));
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
+                for (int nt = 0; nt < NTN; ++nt) {
                     acc[mt][nt] = mfma(ah[mt], b[nt], acc[mt][nt]);
                     acc[mt][nt] = mfma(al[mt], b[nt], acc[mt][nt]);
                 }
         }
     }
+    // every wave is done with the ring before a next chunk refills it
+    q_barrier();
 
     // accumulator element i: row 8 (i / 4) + 4 g2 + i % 4, column l32 of its tile
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const long long c = c0 + 128 * wn + 32 * nt + l32;
+        for (int nt = 0; nt < NTN; ++nt) {
+            const long long c = c0 + 32 * NTN * wn + 32 * nt + l32;
             if (c >= c_end) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -590,6 +586,30 @@ k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ 
                 if (m < g.r) out[(long long)m * g.L + c] = acc[mt][nt][i];
             }
         }
+}
+
+__global__ void __launch_bounds__(512, 1)
+k_bwd_proj(Geo g, const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
+           const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra, const int32_t* __restrict__ n_sel_p,
+           const bf16_t* __restrict__ khi, const bf16_t* __restrict__ klo, const bf16_t* __restrict__ vhi,
+           const bf16_t* __restrict__ vlo, float* __restrict__ dE, float* __restrict__ dF) {
+    __shared__ __attribute__((aligned(16))) char ring[Q_STAGES * Q_STAGE];
+    const int z = blockIdx.z;
+    int ns = *n_sel_p;
+    ns = ns < 0 ? 0 : (ns > g.Kp ? g.Kp : ns);
+    const long long Lh = (long long)ns * g.Tp;
+    float* out = z ? dF : dE;
+    const int nhr = (int)((g.hist_rows + QR - 1) / QR);
+    const bool hist = (int)blockIdx.x < nhr;
+    const long long r0 = hist ? (long long)blockIdx.x * QR : g.hist_rows + (long long)(blockIdx.x - nhr) * QR;
+    const long long part_end = hist ? g.hist_rows : g.L;
+    const long long r1 = r0 + QR < part_end ? r0 + QR : part_end;
+    const int m0 = blockIdx.y * QM;
+    const long long e0 = r0 + 256 < r1 ? r0 + 256 : r1;
+    bwd_proj_chunk<4>(g, ring, z, m0, r0, e0, Lh, hist, k_hist, v_hist, k_intra, v_intra, khi, klo, vhi, vlo, out);
+    if (e0 < r1)
+        bwd_proj_chunk<3>(g, ring, z, m0, e0, r1, Lh, hist, k_hist, v_hist, k_intra, v_intra, khi, klo, vhi, vlo,
+                          out);
 }
 
 // Query slices of the low-rank backward: about one work-group per CU of a
@@ -705,8 +725,8 @@ hipError_t launch_backward_params(const Geo& g, const void* q, const void* k_his
                            (const bf16_t*)w.klf, (const bf16_t*)w.vhf, (const bf16_t*)w.vlf, w.pk, w.pv);
     hipLaunchKernelGGL(k_bwd_lowrank_sum, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, st, (long long)rhd, ns,
                        (const float*)w.pk, (const float*)w.pv, w.dkhi, w.dklo, w.dvhi, w.dvlo);
-    const unsigned tiles = (unsigned)((g.hist_rows + QN - 1) / QN + (g.Lq + QN - 1) / QN);
-    hipLaunchKernelGGL(k_bwd_proj, dim3(tiles, (g.r + QM - 1) / QM, 2), dim3(512), 0, st, g, (const bf16_t*)k_hist,
+    const unsigned ranges = (unsigned)((g.hist_rows + QR - 1) / QR + (g.Lq + QR - 1) / QR);
+    hipLaunchKernelGGL(k_bwd_proj, dim3(ranges, (g.r + QM - 1) / QM, 2), dim3(512), 0, st, g, (const bf16_t*)k_hist,
                        (const bf16_t*)v_hist, (const bf16_t*)k_intra, (const bf16_t*)v_intra, n_sel,
                        (const bf16_t*)w.dkhi, (const bf16_t*)w.dklo, (const bf16_t*)w.dvhi, (const bf16_t*)w.dvlo, d_E,
                        d_F);
