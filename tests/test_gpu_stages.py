@@ -372,6 +372,29 @@ def test_nan_page_scores_rank_last():
         assert np.all(pi[n:] == -1)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nonfinite_query_scores(dtype):
+    """A query holding +inf makes the chunk mean infinite in that column, so
+    every page score is +inf, -inf or NaN by the sign of the page means
+    there: the kernel takes these pages' scores from the exact terms and
+    ranks them as the oracle does (NaN as -inf, ties to the lower page)."""
+    s = synth.shape("tiny").with_(P=12, Kp=4, dtype=dtype, seed=37)
+    ch = synth.draw_chunk(s)
+    q = ch["q"].copy()
+    q[5, 0, 3] = 0x7F80 if dtype == "bf16" else np.float32(np.inf)   # +inf (bfloat16 bits)
+    ch["q"] = q
+    prompts = np.zeros(12, np.int32)
+    c = Case(s, chunk=ch, page_prompt=prompts)
+    km = c.page_summary()
+    kmh = host(km).astype(np.float64)
+    qbar = oracle.chunk_query_mean(oracle.as_f64(ch["q"], s.dtype))
+    assert np.isinf(qbar[0, 3])
+    want, n = oracle.retrieve(kmh, prompts, s.cur_prompt, qbar, s.Kp)
+    page_idx, n_sel, _, _ = c.gather(km)
+    assert int(host(n_sel)[0]) == n
+    assert host(page_idx)[:n].tolist() == want.tolist(), (host(page_idx), want)
+
+
 @pytest.mark.parametrize("policy", ["two_stage", "page_only", "prompt_only", "recent", "random",
                                     "mismatched"])
 @pytest.mark.parametrize("Kp,seed", [(4, 0), (3, 987654321)])
