@@ -186,15 +186,17 @@ HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float 
     mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     const float mt = mx * scale_log2;
     const bool moved = mt > w.m + kLazyMax;
-    const float m_new = moved ? mt : w.m;
-    const float alpha = moved ? fast_exp2(w.m - m_new) : 1.0f;
+    const float m_old = w.m;
+    const float m_new = moved ? mt : m_old;
     w.m = m_new;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_new));
-    // the half's weights are added to the row sum by pv_half, as rounded for the MFMA
-    w.l *= alpha;
-    // rescale O only when some running max of the wave was raised
+    // the half's weights are added to the row sum by pv_half, as rounded for
+    // the MFMA; the row sum and O are rescaled only when some running max of
+    // the wave was raised (the factor is 1 in every other lane)
     if (__builtin_amdgcn_ballot_w64(moved)) {
+        const float alpha = moved ? fast_exp2(m_old - m_new) : 1.0f;
+        w.l *= alpha;
 #pragma unroll
         for (int dt = 0; dt < Wave<D>::DT; ++dt) w.o[dt] *= alpha;
     }
