@@ -161,26 +161,32 @@ struct Wave {
     float m, l;                         // running max (log2 units), this lane's share of the row sum
 };
 
-// Online softmax over one 32-key half of a tile (keys 32 sub..): mask the
-// keys past `nvalid`, update the running max (raised only when a score
-// passes it by more than kLazyMax, so O is rarely rescaled; weights stay
-// below 2^kLazyMax) and the row sum, and turn the scores into weights.
+// Online softmax over a whole 64-key tile, both 32-key halves at once: mask
+// the keys past `nvalid`, update the running max once per tile (raised only
+// when a score passes it by more than kLazyMax, so O is rarely rescaled;
+// weights stay below 2^kLazyMax) and turn the scores into weights. One
+// update per tile rather than per half saves a cross-lane max, a threshold
+// test and their hazard waits per tile.
 template <int D>
-HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float scale_log2) {
+HSAKV_DEV void softmax_tile(Wave<D>& w, f32x16_t (&s)[2], int nvalid, float scale_log2) {
     const int g2 = (threadIdx.x & 63) >> 5;
-    if (nvalid < 32 * (sub + 1)) {
-        // element i holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4: valid below t
-        const int t = nvalid - 32 * sub - 4 * g2;
+    if (nvalid < 64) {
+        // element i of half sub holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4: valid below t
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < t ? s[i] : -INFINITY;
+        for (int sub = 0; sub < 2; ++sub) {
+            const int t = nvalid - 32 * sub - 4 * g2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[sub][i] = 8 * (i >> 2) + (i & 3) < t ? s[sub][i] : -INFINITY;
+        }
     }
     // raw scores: the max is taken before scaling (scale > 0), and the scale
     // folds into the exponent's FMA. The NaN-propagating maximum maps to a
     // chain of three-input max instructions with no operand quieting (a NaN
     // score makes its row NaN either way, through its own weight)
-    float mx = s[0];
+    float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[i]);
+    for (int i = 1; i < 16; ++i)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][i], s[1][i]));
     // lanes l and l + 32 hold the two key quarters of the same query
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -190,10 +196,12 @@ HSAKV_DEV void softmax_half(Wave<D>& w, f32x16_t& s, int sub, int nvalid, float 
     const float m_new = moved ? mt : m_old;
     w.m = m_new;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_new));
-    // the half's weights are added to the row sum by pv_half, as rounded for
-    // the MFMA; the row sum and O are rescaled only when some running max of
-    // the wave was raised (the factor is 1 in every other lane)
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[sub][i] = fast_exp2(fmaf(s[sub][i], scale_log2, -m_new));
+    // the weights are added to the row sum by pv_half, as rounded for the
+    // MFMA; the row sum and O are rescaled only when some running max of the
+    // wave was raised (the factor is 1 in every other lane)
     if (__builtin_amdgcn_ballot_w64(moved)) {
         const float alpha = moved ? fast_exp2(m_old - m_new) : 1.0f;
         w.l *= alpha;
@@ -262,9 +270,9 @@ HSAKV_DEV void pv_half(Wave<D>& w, const f32x16_t& s, const char* vt, int sub) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
 }
 
-// One 64-key tile as two 32-key online-softmax steps. The order S(0), S(1),
-// softmax(0), PV(0), softmax(1), PV(1) lets the matrix cores run S(1) and
-// PV(0) while the vector ALUs work on the softmax of the other half.
+// One 64-key tile: S of both 32-key halves, one online-softmax step over the
+// 64 keys, then P V of both halves. The VALU block of one wave runs beside
+// the matrix work of the other wave on its SIMD.
 template <int D>
 HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid, float scale_log2) {
     using LY = Lay<D>;
@@ -294,9 +302,8 @@ HSAKV_DEV void tile_step(Wave<D>& w, const char* kt, const char* vt, int nvalid,
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-    softmax_half<D>(w, s[0], 0, nvalid, scale_log2);
+    softmax_tile<D>(w, s, nvalid, scale_log2);
     pv_half<D>(w, s[0], vt, 0);
-    softmax_half<D>(w, s[1], 1, nvalid, scale_log2);
     pv_half<D>(w, s[1], vt, 1);
 }
 
