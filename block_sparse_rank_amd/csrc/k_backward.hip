@@ -679,42 +679,37 @@ hipError_t launch_backward_params(const Geo& g, const void* q, const void* k_his
     const int ns = lowrank_slices(g);
     const bool split = side != st;
     hipError_t e = hipSuccess;
-    // the side stream starts once the inputs are ready on the main stream
-    if (split && (e = hipEventRecord(ev_fork, st)) == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
-    if (e != hipSuccess) return e;
 
-    // side: K', V' split and the log-sum-exp (inputs only)
-    hipLaunchKernelGGL(k_bwd_split, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, side, (long long)rhd, k_low,
+    // main: the K', V' split, the log-sum-exp and the gate terms, one after
+    // another (on two streams they slowed each other down, and the low-rank
+    // backward needs all three)
+    hipLaunchKernelGGL(k_bwd_split, dim3((unsigned)((rhd + 255) / 256)), dim3(256), 0, st, (long long)rhd, k_low,
                        v_low, w.khf, w.klf, w.vhf, w.vlf);
     const dim3 lse_grid((g.Lq + 255) / 256, g.H), low_grid((g.r + kKeyGroup - 1) / kKeyGroup, g.H, ns);
     if (g.d == 128)
-        hipLaunchKernelGGL(k_bwd_lse<128>, lse_grid, dim3(256), 0, side, g, qb, (const bf16_t*)w.khf,
+        hipLaunchKernelGGL(k_bwd_lse<128>, lse_grid, dim3(256), 0, st, g, qb, (const bf16_t*)w.khf,
                            (const bf16_t*)w.klf, w.lse);
     else
-        hipLaunchKernelGGL(k_bwd_lse<64>, lse_grid, dim3(256), 0, side, g, qb, (const bf16_t*)w.khf,
+        hipLaunchKernelGGL(k_bwd_lse<64>, lse_grid, dim3(256), 0, st, g, qb, (const bf16_t*)w.khf,
                            (const bf16_t*)w.klf, w.lse);
-    if (split && (e = hipEventRecord(ev_join, side)) != hipSuccess) return e;
-
-    // main: the gate terms
     if (g.d == 128)
         hipLaunchKernelGGL(k_bwd_gate<128>, dim3((unsigned)((th + 15) / 16)), dim3(256), 0, st, g, qb, w_g, b_g, o_s,
                            o_l, (const bf16_t*)d_out, w.dx, w.dohi, w.dolo, w.Dt);
     else
         hipLaunchKernelGGL(k_bwd_gate<64>, dim3((unsigned)((th + 31) / 32)), dim3(256), 0, st, g, qb, w_g, b_g, o_s,
                            o_l, (const bf16_t*)d_out, w.dx, w.dohi, w.dolo, w.Dt);
-
-    // side: the gate-parameter sums, once dx is there
+    // side: the gate-parameter sums, once dx is there, beside the low-rank
+    // backward and dE, dF (nothing after them on the main stream needs them)
     if (split && (e = hipEventRecord(ev_fork, st)) == hipSuccess) e = hipStreamWaitEvent(side, ev_fork, 0);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_bwd_gate_part, dim3(g.H, kGateSlices), dim3(256), 0, side, g, qb, (const float*)w.dx, w.pw,
                        w.pb);
     hipLaunchKernelGGL(k_bwd_gate_fin, dim3(g.H), dim3(128), 0, side, g, (const float*)w.pw, (const float*)w.pb,
                        d_wg, d_bg);
+    if (split && (e = hipEventRecord(ev_join, side)) != hipSuccess) return e;
 
-    // main: the low-rank backward after the log-sum-exp (the first join
-    // record), then dE and dF; the second join record covers the sums
-    if (split && (e = hipStreamWaitEvent(st, ev_join, 0)) == hipSuccess) e = hipEventRecord(ev_join, side);
-    if (e != hipSuccess) return e;
+    // main: the low-rank backward, its slice sum, then dE and dF; the call's
+    // stream waits for the sums at the end
     if (g.d == 128)
         hipLaunchKernelGGL(k_bwd_lowrank<128>, low_grid, dim3(256), 0, st, g, ns, qb, (const bf16_t*)w.dohi,
                            (const bf16_t*)w.dolo, (const float*)w.lse, (const float*)w.Dt, (const bf16_t*)w.khf,

@@ -410,9 +410,9 @@ int hsa_forward(const hsakv_dims* dims, const float* tau, int32_t cur_prompt,
  * [Lq][H][d]). bf16 only (float32 data returns HSAKV_ERR_BAD_DTYPE);
  * (Kp Tp + Lq) H d 2 bytes must stay below 2^31 (else HSAKV_ERR_UNSUPPORTED).
  * Workspace: HSAKV_ENTRY_BACKWARD. `fork` (host, nullable): with a fork
- * whose stream is set, the log-sum-exp and the gate-parameter sums run on
- * the fork's stream beside the gate terms and the low-rank backward; NULL
- * runs everything on `stream`. Every reduction runs in a fixed order: the
+ * whose stream is set, the gate-parameter sums run on the fork's stream
+ * beside the low-rank backward and dE, dF; NULL runs everything on
+ * `stream`. Every reduction runs in a fixed order: the
  * results are the same bits from run to run, with or without a fork. */
 int hsa_backward_params(const hsakv_dims* dims, const void* q, const void* k_hist, const void* v_hist,
                         const void* k_intra, const void* v_intra, const int32_t* n_sel, const float* w_g,
