@@ -255,8 +255,13 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 // and each key slice once per 256 rows of E (half and a quarter of the L2
 // reads of 128 x 128 tiles), and each of the 256 E rows of a step is one
 // whole 128-byte line. 8 waves (wave w: rows 128 (w % 2), columns 64 (w / 2),
-// eight 32x32 accumulators), one work-group per CU and two 64 KB LDS stages,
-// the next step's DMA in flight during a step's MFMA work. The 16-byte chunks
+// eight 32x32 accumulators) and one work-group per CU. The LDS is a ring of
+// five 32 KB half-stages, each the X (E or F) tile or the Y (keys or values)
+// tile of one k-step, sent in the order X0 Y0 X1 Y1 X2 ...: a half-stage is
+// refilled as soon as the step that used it is done, so during the MFMA work
+// of step i the halves X(i+1), Y(i+1) and X(i+2) are in flight (1.5 steps,
+// where two 64 KB stages hold one; the 160 KB of LDS do not fit three). The
+// 16-byte chunks
 // of a row are XOR-swizzled in LDS for conflict-free operand reads, with rows
 // unpadded so every DMA lane loads data and each row's bytes stay contiguous:
 // X (128-byte rows) slot s of row r holds chunk s ^ (r / 2 mod 8), so the 16
@@ -269,20 +274,23 @@ k_lowrank_proj32(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict__
 // through buffer loads whose resource covers exactly the valid bytes: a Y row
 // past the part's end, or an X column past the end of E, is out of range and
 // not read; its LDS row is zeroed before use.
-constexpr int WM = 256, WN = 256, WK = 64, WT = 512, WWV = 8, WSTAGES = 2;
+constexpr int WM = 256, WN = 256, WK = 64, WT = 512, WWV = 8;
 constexpr int WA_SLOTS = WK / 8;               // 8 chunks per X row
 constexpr int WB_SLOTS = WN / 8;               // 32 chunks per Y row
 constexpr int WA_ROWB = WA_SLOTS * 16;         // 128
 constexpr int WB_ROWB = WB_SLOTS * 16;         // 512
 constexpr int WA_BYTES = WM * WA_ROWB;         // 32768
 constexpr int WB_BYTES = WK * WB_ROWB;         // 32768
-constexpr int WSTAGE = WA_BYTES + WB_BYTES;    // 65536; two stages 131072 bytes
+constexpr int WHALF = 32768;                   // one half-stage: an X or a Y tile
+constexpr int WRING = 5;                       // half-stages in the ring (160 KB)
 constexpr int WA_INSTR = WM * WA_SLOTS / 64;   // 32
 constexpr int WB_INSTR = WK * WB_SLOTS / 64;   // 32
 constexpr int W_PER = 8;                       // DMA instructions per wave and k-step
 static_assert(WM * WA_SLOTS % 64 == 0 && WK * WB_SLOTS % 64 == 0, "whole wave instructions");
+static_assert(WA_BYTES == WHALF && WB_BYTES == WHALF, "X and Y tiles fill one half-stage each");
 static_assert(WA_BYTES == WA_INSTR * 1024, "Y follows X in instruction order");
 static_assert(WA_INSTR + WB_INSTR == WWV * W_PER, "every wave sends the same count");
+static_assert(WA_INSTR == 4 * WWV && WB_INSTR == 4 * WWV, "four DMA instructions per wave and half-stage");
 HSAKV_DEV int xswz(int row) { return (row >> 1) & 7; }   // X chunk swizzle
 HSAKV_DEV int yswz(int row) { return 4 * (row & 3); }    // Y chunk swizzle
 
@@ -301,7 +309,12 @@ HSAKV_DEV lds_void_t* w_dst(char* p) {
     return (lds_void_t*)(uintptr_t)__builtin_amdgcn_readfirstlane(v);
 }
 
-HSAKV_DEV void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt vmcnt(N) with the other counters unconstrained.
+template <int N>
+HSAKV_DEV void wait_vm() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // LDS-only work-group barrier (DMA in flight stays in flight).
 HSAKV_DEV void w_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -324,11 +337,11 @@ HSAKV_DEV void w_lanes(uint32_t (&off)[W_PER], const Geo& g, int wave, int m0, i
     }
 }
 
-// Zero the Y rows [first, WK) of a stage.
-HSAKV_DEV void w_zero_tail(char* buf, int first) {
+// Zero the rows [first, WK) of a Y tile.
+HSAKV_DEV void w_zero_tail(char* yb, int first) {
     for (int idx = threadIdx.x; idx < (WK - first) * (WN / 8); idx += WT) {
         const int row = first + idx / (WN / 8), c = idx % (WN / 8);
-        *reinterpret_cast<uint4*>(buf + WA_BYTES + row * WB_ROWB + c * 16) = uint4{0, 0, 0, 0};
+        *reinterpret_cast<uint4*>(yb + row * WB_ROWB + c * 16) = uint4{0, 0, 0, 0};
     }
 }
 
@@ -338,18 +351,18 @@ typedef __attribute__((ext_vector_type(2))) unsigned w_u32x2_t;
 // transpose reads of Y sit in one asm block that waits for them itself:
 // issued as builtins, they would make the compiler wait for every DMA in
 // flight first (the next step's included).
-HSAKV_DEV void w_compute(const char* buf, f32x16_t (&acc)[4][2], int wave, int h) {
+HSAKV_DEV void w_compute(const char* xb, const char* yb, f32x16_t (&acc)[4][2], int wave, int h) {
     const int lane = threadIdx.x & 63;
     const int mw = wave & 1, nw = wave >> 1;
     const int r32 = lane & 31, g2 = lane >> 5, G = lane >> 4, j = lane & 15;
     // X row 128 mw + 32 mt + r32 has swizzle xswz(r32); chunk 4 h + 2 kk + g2 sits in slot chunk ^ xswz
-    const char* Arow = buf + (128 * mw + r32) * WA_ROWB;
+    const char* Arow = xb + (128 * mw + r32) * WA_ROWB;
     const char* A0 = Arow + 16 * ((4 * h + g2) ^ xswz(r32));
     const char* A1 = Arow + 16 * ((4 * h + 2 + g2) ^ xswz(r32));
     // Y rows 32 h + 16 kk + 4 e + 8 (G / 2) + j / 4 have swizzle yswz(j / 4); the 8 columns of
     // chunk 8 nw + 4 nt + 2 (G & 1) + (j & 3) / 2 sit in slot chunk ^ yswz, at byte 8 (j & 1)
     const int cy = 8 * nw + 2 * (G & 1) + ((j & 3) >> 1);
-    const char* Brow = buf + WA_BYTES + (32 * h + 8 * (G >> 1) + (j >> 2)) * WB_ROWB + 8 * (j & 1);
+    const char* Brow = yb + (32 * h + 8 * (G >> 1) + (j >> 2)) * WB_ROWB + 8 * (j & 1);
     const uint32_t bb0 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * (cy ^ yswz(j >> 2)));
     const uint32_t bb1 = (uint32_t)(uintptr_t)(const lds_i16x4_t*)(Brow + 16 * ((cy + 4) ^ yswz(j >> 2)));
     // r[4 kk + 2 nt + e]: k rows 16 kk + 4 e (+ 8 (G / 2) + j / 4), columns 32 nt + ...
@@ -397,7 +410,7 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
                   const bf16_t* __restrict__ k_hist, const bf16_t* __restrict__ v_hist,
                   const bf16_t* __restrict__ k_intra, const bf16_t* __restrict__ v_intra,
                   const int32_t* __restrict__ n_sel_p, int nsplit, int per_xcd, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) char ring[WSTAGES * WSTAGE];
+    __shared__ __attribute__((aligned(16))) char ring[WRING * WHALF];
     const int MT = (g.r + WM - 1) / WM, NTL = g.HD / WN;
     const int total = nsplit * 2 * MT * NTL;
     const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -428,25 +441,32 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
     w_lanes(off, g, wave, m0, n0);
     const long long xbytes = 2LL * g.r * g.L;
 
-    // Send k-step s into its stage: per instruction a uniform resource (X or
-    // Y) and LDS target.
-    auto send = [&](int s) __attribute__((always_inline)) {
-        if (s >= n) return;
+    // Send half-stage hh (X of k-step hh / 2 when hh is even, Y when odd)
+    // into ring slot hh % WRING: four DMA instructions per wave, each with a
+    // uniform resource and LDS target.
+    auto send = [&](int hh) __attribute__((always_inline)) {
+        const int s = hh >> 1;
         const bool hist = s < nh;
         const long long k = hist ? kb + (long long)s * WK : cb + (long long)(s - nh) * WK;
-        const long long end = hist ? he : ke;
-        const long long col = hist ? k : g.hist_rows + (k - Lh);
-        const bf16_t* yb = hist ? Yh + k * g.HD : Yc + (k - Lh) * g.HD;
-        const int rows = end - k < WK ? (int)(end - k) : WK;
-        const __amdgpu_buffer_rsrc_t rx = w_rsrc(X + col, xbytes - 2 * col);
-        const __amdgpu_buffer_rsrc_t ry = w_rsrc(yb, 2LL * rows * g.HD);
-        char* buf = ring + (s & 1) * WSTAGE;
+        char* buf = ring + (hh % WRING) * WHALF;
+        if ((hh & 1) == 0) {
+            const long long col = hist ? k : g.hist_rows + (k - Lh);
+            const __amdgpu_buffer_rsrc_t rx = w_rsrc(X + col, xbytes - 2 * col);
 #pragma unroll
-        for (int q = 0; q < W_PER; ++q) {
-            const int j = wave + WWV * q;
-            const __amdgpu_buffer_rsrc_t rs = j < WA_INSTR ? rx : ry;
-            char* dst = buf + j * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, w_dst(dst), 16, off[q], 0, 0, 0);
+            for (int q = 0; q < 4; ++q) {
+                const int j = wave + WWV * q;   // X instruction j < WA_INSTR
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, w_dst(buf + j * 1024), 16, off[q], 0, 0, 0);
+            }
+        } else {
+            const long long end = hist ? he : ke;
+            const bf16_t* yb = hist ? Yh + k * g.HD : Yc + (k - Lh) * g.HD;
+            const int rows = end - k < WK ? (int)(end - k) : WK;
+            const __amdgpu_buffer_rsrc_t ry = w_rsrc(yb, 2LL * rows * g.HD);
+#pragma unroll
+            for (int q = 4; q < W_PER; ++q) {
+                const int j = wave + WWV * q - WA_INSTR;   // Y instruction j
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, w_dst(buf + j * 1024), 16, off[q], 0, 0, 0);
+            }
         }
     };
 
@@ -456,24 +476,38 @@ k_lowrank_proj256(Geo g, const bf16_t* __restrict__ E, const bf16_t* __restrict_
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16_t{};
 
-    send(0);
+    const int halves = 2 * n;
+    int sent = halves < WRING ? halves : WRING;
+    for (int hh = 0; hh < sent; ++hh) send(hh);
 #pragma unroll 1
     for (int i = 0; i < n; ++i) {
-        // step i is the only one in flight; the barrier also retires every
-        // wave's reads of the other stage (step i - 1), which step i + 1 refills
-        wait_vm0();
+        // halves 2i and 2i + 1 have landed once at most the halves sent after
+        // them are outstanding (four DMA instructions per wave each); the
+        // barrier makes every wave's part visible and retires every read of
+        // step i - 1, whose two slots are then refilled
+        const int later = sent - (2 * i + 2);
+        if (later >= 3)
+            wait_vm<12>();
+        else if (later == 2)
+            wait_vm<8>();
+        else if (later == 1)
+            wait_vm<4>();
+        else
+            wait_vm<0>();
         w_barrier();
-        char* now = ring + (i & 1) * WSTAGE;
+        const char* xb = ring + ((2 * i) % WRING) * WHALF;
+        char* yb = ring + ((2 * i + 1) % WRING) * WHALF;
         const bool hist = i < nh;
         const long long k = hist ? kb + (long long)i * WK : cb + (long long)(i - nh) * WK;
         const long long end = hist ? he : ke;
         if (end - k < WK) {   // the last, partial step of a part
-            w_zero_tail(now, (int)(end - k));
+            w_zero_tail(yb, (int)(end - k));
             w_barrier();
         }
-        send(i + 1);
-        w_compute(now, acc, wave, 0);
-        w_compute(now, acc, wave, 1);
+        // a half may be sent once the half WRING before it is consumed
+        while (sent < halves && sent < 2 * i + WRING) send(sent++);
+        w_compute(xb, yb, acc, wave, 0);
+        w_compute(xb, yb, acc, wave, 1);
     }
 
     const int lane = threadIdx.x & 63;
