@@ -865,6 +865,14 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
     const int query = i * g.Bq + 32 * (wave & 1) + (lane & 31);
     const bool ok = i < g.NQB && query < g.Lq;
     __shared__ float gpart[DT][64];
+    // the low-rank output this thread blends, loaded first so that its
+    // latency overlaps that of the partials
+    float4 lin[4] = {};
+    if (ep.out && ok) {
+        const float* lp = ep.o_lin + (long long)query * g.HD + (long long)h * D + 32 * dt + 4 * g2;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) lin[a] = *reinterpret_cast<const float4*>(lp + 8 * a);
+    }
     if (ep.out) {
         float dot = 0.f;
         if (ok) {
@@ -931,11 +939,10 @@ k_sparse_combine(Geo g, const bf16_t* __restrict__ q, const int32_t* __restrict_
         const float4 r = {o[4 * a] * inv_l, o[4 * a + 1] * inv_l, o[4 * a + 2] * inv_l, o[4 * a + 3] * inv_l};
         if (ep.o_main) *reinterpret_cast<float4*>(ep.o_main + base + d0) = r;
         if (ep.out) {
-            const float4 lin = *reinterpret_cast<const float4*>(ep.o_lin + base + d0);
-            const float r0 = gate * r.x + (1.f - gate) * lin.x;
-            const float r1 = gate * r.y + (1.f - gate) * lin.y;
-            const float r2 = gate * r.z + (1.f - gate) * lin.z;
-            const float r3 = gate * r.w + (1.f - gate) * lin.w;
+            const float r0 = gate * r.x + (1.f - gate) * lin[a].x;
+            const float r1 = gate * r.y + (1.f - gate) * lin[a].y;
+            const float r2 = gate * r.z + (1.f - gate) * lin[a].z;
+            const float r3 = gate * r.w + (1.f - gate) * lin[a].w;
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16(r0) | ((uint32_t)f32_to_bf16(r1) << 16);
             pk.y = (uint32_t)f32_to_bf16(r2) | ((uint32_t)f32_to_bf16(r3) << 16);
