@@ -48,7 +48,8 @@ VARIANTS = [
     # two row tiles, the second ragged
     ("bf16-r320-hd256", _variant("tiny", dtype="bf16", H=4, d=64, r=320, Lq=136, tokens_per_frame=13,
                                  P=8, Kp=3, clustered=True, tau_law="uniform", seed=26), {}),
-    # three 64-key steps per split (the two-stage LDS ring wraps), a split across the seam
+    # three and four 64-key steps per split (the ring of five half-stages wraps), a split across the seam;
+    # with r128-seam and r320-hd256 (one and two steps) every fill state of the ring
     ("bf16-r128-long", _variant("tiny", dtype="bf16", H=2, d=128, r=128, Lq=1000, tokens_per_frame=250,
                                 clustered=True, tau_law="uniform", seed=27), {}),
     # eight slots out of 24 pages: the retrieval's slot order over more chosen pages
