@@ -26,9 +26,10 @@
 //   e < 4: key 16c + 4(l/32) + e,   e >= 4: key 16c + 8 + 4(l/32) + e - 4
 // and the V^T operand comes in the same key order from ds_read_b64_tr_b16
 // transpose reads of the row-major V tile, so P never leaves its lane. Each
-// half is one online-softmax step (float32, exp2 with the log2(e)/sqrt(d)
-// scale folded into the exponent's FMA); the row sum is taken on the bf16
-// weights the MFMA consumes.
+// 64-key tile is one online-softmax step (float32, exp2 with the log2(e)/
+// sqrt(d) scale folded into the exponent's FMA; the running max raised only
+// when a score passes it by more than 8 in log2 units, so O is rarely
+// rescaled); the row sum is taken on the bf16 weights the MFMA consumes.
 #include "common.h"
 #include "launch.h"
 
@@ -129,82 +130,146 @@ HSAKV_DEV void lwait_vmcnt() {
 
 HSAKV_DEV void llds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One 32-key half: masking past nvalid, online softmax, O^T += V^T P^T for
-// both V parts.
+constexpr float kLazyMaxL = 8.0f;   // margin (log2 units) before the running max is raised
+constexpr int kSchedMfmaL = 0x008, kSchedDsReadL = 0x100;
+
+typedef __attribute__((ext_vector_type(2))) float lf32x2_t;
+
+// O^T += V^T P^T over one 32-key half for both V parts, P^T from the half's
+// weights (bf16, as the MFMA takes them), which are also added to this lane's
+// share of the row sum. The V^T operands are read four reads ahead of their
+// MFMAs.
 template <int D>
-HSAKV_DEV void lhalf(LWave<D>& w, f32x16_t& s, const char* buf, int sub, int nvalid, float scale_log2) {
+HSAKV_DEV void lpv_half(LWave<D>& w, const f32x16_t& s, const char* buf, int sub) {
     using LY = LLay<D>;
+    constexpr int DT = LY::DT;
     const int lane = threadIdx.x & 63;
-    const int g2 = lane >> 5, G = lane >> 4, j = lane & 15;
-    if (nvalid < 32 * (sub + 1)) {
-        const int t = nvalid - 32 * sub - 4 * g2;   // element i holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4
+    const int G = lane >> 4, j = lane & 15;
+    bf16x2_t pp[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 8 * (i >> 2) + (i & 3) < t ? s[i] : -INFINITY;
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    // a half of a tile can hold no valid key at all (mx = -inf): no change then
-    const float mt = mx * scale_log2;
-    const float m_new = fmaxf(w.m, mt);
-    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(w.m - m_new);
-    w.m = m_new;
+    for (int i = 0; i < 8; ++i) pp[i] = __builtin_convertvector((lf32x2_t){s[2 * i], s[2 * i + 1]}, bf16x2_t);
     bf16x8_t pf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        pf[c] = __builtin_shufflevector(__builtin_shufflevector(pp[4 * c], pp[4 * c + 1], 0, 1, 2, 3),
+                                        __builtin_shufflevector(pp[4 * c + 2], pp[4 * c + 3], 0, 1, 2, 3),
+                                        0, 1, 2, 3, 4, 5, 6, 7);
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs = w.l * alpha;
+    float rs = w.l;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            pf[c][e] = (__bf16)(m_new == -INFINITY ? 0.f : fast_exp2(fmaf(s[8 * c + e], scale_log2, -m_new)));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{pf[c][2 * e], pf[c][2 * e + 1]}, ones, rs, false);
-    }
+    for (int i = 0; i < 8; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(pp[i], ones, rs, false);
     w.l = rs;
-#pragma unroll
-    for (int dt = 0; dt < LY::DT; ++dt) w.o[dt] *= alpha;
+    i16x4_t lo[2][DT][2], hi[2][DT][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         const int krow = 32 * sub + 16 * c + 4 * (G >> 1) + (j >> 2);
 #pragma unroll
-        for (int dt = 0; dt < LY::DT; ++dt) {
+        for (int dt = 0; dt < DT; ++dt) {
             const int off = krow * LY::VP + 2 * (32 * dt + 16 * (G & 1) + 4 * (j & 3));
 #pragma unroll
             for (int part = 0; part < 2; ++part) {
                 const char* vt = buf + (part ? LY::VLO : LY::VHI);
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off));
-                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off + 8 * LY::VP));
-                const i16x8_t vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                w.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[c], w.o[dt],
-                                                                  0, 0, 0);
+                lo[c][dt][part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off));
+                hi[c][dt][part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vt + off + 8 * LY::VP));
             }
         }
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                const i16x8_t vv = __builtin_shufflevector(lo[c][dt][part], hi[c][dt][part], 0, 1, 2, 3, 4, 5, 6, 7);
+                w.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[c], w.o[dt],
+                                                                  0, 0, 0);
+            }
+    // 4 reads ahead, then one MFMA per two reads, then the last two MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsReadL, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 4 * DT - 2; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfmaL, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsReadL, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfmaL, 2, 0);
 }
 
+// One 64-key tile: S^T = K'_hi Q^T + K'_lo Q^T for both 32-key halves (K
+// operands read four MFMAs ahead), one online-softmax step over the 64 keys
+// (keys past nvalid masked; the running max is raised only when a score
+// passes it by more than kLazyMaxL, so O is rarely rescaled and the weights
+// stay below 2^kLazyMaxL), then P V of both halves. A half with no valid key
+// has no products.
 template <int D>
 HSAKV_DEV void ltile(LWave<D>& w, const char* buf, int nvalid, float scale_log2) {
     using LY = LLay<D>;
+    constexpr int KS = LY::KS;
     const int lane = threadIdx.x & 63;
     const int r32 = lane & 31, g2 = lane >> 5;
+    bf16x8_t ah[2][KS], al[2][KS];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        const char* kr = buf + (32 * sub + r32) * LY::KP + 16 * g2;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ah[sub][ks] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
+            al[sub][ks] = *reinterpret_cast<const bf16x8_t*>(kr + LY::KLO + 32 * ks);
+        }
+    }
     f32x16_t s[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
         s[sub] = f32x16_t{};
-        const char* kr = buf + (32 * sub + r32) * LY::KP + 16 * g2;
 #pragma unroll
-        for (int ks = 0; ks < LY::KS; ++ks) {
-            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(kr + 32 * ks);
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(kr + LY::KLO + 32 * ks);
-            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, w.qf[ks], s[sub], 0, 0, 0);
-            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, w.qf[ks], s[sub], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[sub][ks], w.qf[ks], s[sub], 0, 0, 0);
+            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[sub][ks], w.qf[ks], s[sub], 0, 0, 0);
         }
     }
-    lhalf<D>(w, s[0], buf, 0, nvalid, scale_log2);
-    if (nvalid > 32) lhalf<D>(w, s[1], buf, 1, nvalid, scale_log2);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsReadL, 4, 0);
+#pragma unroll
+    for (int m = 0; m < 4 * KS - 4; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfmaL, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsReadL, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfmaL, 4, 0);
+    if (nvalid < 64) {
+        // element i of half sub holds key 32 sub + 4 g2 + 8 (i / 4) + i % 4: valid below t
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int t = nvalid - 32 * sub - 4 * g2;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[sub][i] = 8 * (i >> 2) + (i & 3) < t ? s[sub][i] : -INFINITY;
+        }
+    }
+    // raw scores: the max is taken before scaling (scale > 0); NaN-propagating
+    // three-input maxima (a NaN score makes its row NaN either way)
+    float mx = __builtin_elementwise_maximum(s[0][0], s[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[0][i], s[1][i]));
+    // lanes l and l + 32 hold the two key quarters of the same query
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float mt = mx * scale_log2;
+    const bool moved = mt > w.m + kLazyMaxL;
+    const float m_old = w.m;
+    const float m_new = moved ? mt : m_old;
+    w.m = m_new;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[sub][i] = fast_exp2(fmaf(s[sub][i], scale_log2, -m_new));
+    // the row sum and O are rescaled only when some running max of the wave
+    // was raised (the factor is 1 in every other lane; 0 on the first tile)
+    if (__builtin_amdgcn_ballot_w64(moved)) {
+        const float alpha = moved ? fast_exp2(m_old - m_new) : 1.0f;
+        w.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < LY::DT; ++dt) w.o[dt] *= alpha;
+    }
+    lpv_half<D>(w, s[0], buf, 0);
+    if (nvalid > 32) lpv_half<D>(w, s[1], buf, 1);
 }
 
 template <int D>
