@@ -59,6 +59,7 @@ Geo make_geo(const hsakv_dims* d) {
     g.NB_max = g.NBh_max + g.NBc;
     g.L = g.hist_rows + d->Lq;
     g.elt = d->dtype == HSAKV_BF16 ? 2 : 4;
+    g.one_range = 0;
     return g;
 }
 
@@ -287,6 +288,11 @@ HSAKV_API size_t hsakv_workspace_bytes(const hsakv_dims* dims, int32_t entry) {
         case HSAKV_ENTRY_SUMMARY: return align_up(page_means_ws_bytes(g, g.P));
         case HSAKV_ENTRY_COMMIT: return align_up(page_means_ws_bytes(g, g.Lq / g.Tp + 1));
         case HSAKV_ENTRY_BACKWARD: return align_up(backward_ws_bytes(g));
+        case HSAKV_ENTRY_SPARSE_STATIC: {
+            Geo g1 = g;
+            g1.one_range = 1;
+            return ws_sparse(g1);
+        }
         default: return 0;
     }
 }
@@ -693,7 +699,10 @@ HSAKV_API int hsa_sparse_attn_static(const hsakv_dims* dims, const void* q, cons
                       aligned(v_intra) && aligned(o_sparse) && aligned(n_sel, 4) &&
                       aligned(sel_count, 4) && aligned(sel_idx, 4),
                   HSAKV_ERR_MISALIGNED);
-    const Geo g = make_geo(dims);
+    // one split range per work-group: the partials of the several ranges per
+    // work-group that hsa_sparse_attn runs for the largest heads would not fit
+    Geo g = make_geo(dims);
+    g.one_range = 1;
     if (ws_sparse(g) > (size_t)HSAKV_STATIC_SCRATCH_BYTES) return HSAKV_ERR_TOO_LARGE;
     void* ws = static_scratch();
     if (!ws) return HSAKV_ERR_HIP;

@@ -23,6 +23,7 @@ struct Geo {
     long long hist_rows;  // Kp * Tp
     long long L;          // Kp * Tp + Lq: columns of E and F
     int elt;              // bytes per element of the storage type (2 bf16, 4 f32)
+    int one_range;        // nonzero: the bf16 sparse attention runs one split range per work-group
 };
 
 // Where a page's rows are read from. Without a page table (page_slot null)

@@ -50,6 +50,7 @@ ENTRY_FORWARD = 6
 ENTRY_SUMMARY = 7
 ENTRY_COMMIT = 8
 ENTRY_BACKWARD = 9
+ENTRY_SPARSE_STATIC = 10
 
 EXPORTS = [
     "hsakv_version", "hsakv_status_str", "hsakv_last_hip_error", "hsakv_validate",

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HSAKV_VERSION 5
+#define HSAKV_VERSION 6
 
 /* status codes */
 #define HSAKV_OK                   0
@@ -98,6 +98,7 @@ extern "C" {
 #define HSAKV_ENTRY_SUMMARY  7
 #define HSAKV_ENTRY_COMMIT   8   /* enough for a commit of up to Lq tokens */
 #define HSAKV_ENTRY_BACKWARD 9
+#define HSAKV_ENTRY_SPARSE_STATIC 10  /* scratch hsa_sparse_attn_static uses of its fixed array */
 
 /* Sizes of one chunk-layer; all host integers. Supported: d in {64, 128};
  * Bq = 64; Binter and Bintra multiples of 64 up to 512; r a multiple of 32
@@ -345,8 +346,13 @@ int hsa_sparse_compute(const hsakv_dims* dims, const void* q, const void* k_hist
  * layouts and results are those of hsa_sparse_attn (the same kernels).
  * Scratch: a fixed array of HSAKV_STATIC_SCRATCH_BYTES in device memory,
  * one per GPU, held until the process ends; dims whose plan and partials
- * need more (hsakv_workspace_bytes(dims, HSAKV_ENTRY_SPARSE) larger than
- * that) return HSAKV_ERR_TOO_LARGE before anything is enqueued. The first
+ * need more (hsakv_workspace_bytes(dims, HSAKV_ENTRY_SPARSE_STATIC) larger
+ * than that) return HSAKV_ERR_TOO_LARGE before anything is enqueued. For
+ * more than 8 heads with over 1024 key tiles per group of four query blocks
+ * (over 64K history keys per head), hsa_sparse_attn gives each work-group
+ * several split ranges; this entry keeps one, so that its partials fit, and
+ * its output then differs from hsa_sparse_attn's by float rounding only
+ * (the split points of the online softmax differ). The first
  * call on a device looks up that device's copy of the array (no
  * allocation). Every call on a GPU shares its array and leaves its contents
  * behind; nothing in it must start at zero. Calls that overlap in time on

@@ -71,6 +71,10 @@ VARIANTS = [
     ("bf16-consecutive-rows", _variant("tiny", dtype="bf16", H=1, d=64, Lq=16448, tokens_per_frame=16, Kp=1,
                                        P=2, r=64, clustered=True, tau_law="uniform", seed=33),
      dict(tau=[0.35])),
+    # nine heads and 1032 tiles per group: the attention runs two split ranges
+    # per work-group (more than 1024 tiles per group and more than 8 heads)
+    ("bf16-two-ranges", _variant("tiny", dtype="bf16", H=9, d=64, Lq=512, tokens_per_frame=2048, Kp=4, P=6,
+                                 Binter=64, r=64, clustered=True, tau_law="uniform", seed=35), {}),
 ]
 
 

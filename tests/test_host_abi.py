@@ -24,6 +24,13 @@ def _dims(**over):
     return hs.make_dims(**base)
 
 
+def _shape_dims(name):
+    import synth
+    s = synth.shape(name)
+    return hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize, P=s.P,
+                        Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r, dtype=s.dtype)
+
+
 def test_header_declares_exactly_the_exports():
     with open(os.path.join(ROOT, "include", "hsakv.h")) as f:
         hdr = f.read()
@@ -38,7 +45,7 @@ def test_header_declares_exactly_the_exports():
 
 
 def test_version_and_status_strings():
-    assert hs.version() == 5
+    assert hs.version() == 6
     for code in range(-9, 1):
         assert hs.status_str(code) and hs.status_str(code) != "unknown status"
     assert hs.status_str(-99) == "unknown status"
@@ -99,15 +106,16 @@ def test_static_sparse_rejects_what_exceeds_its_scratch():
     need more than its fixed scratch, on the host, before any launch."""
     big = _dims(H=96, Lq=10800, tokens_per_frame=3600, Kp=6, r=512)
     assert hs.validate(big) == hs.OK
-    assert hs.workspace_bytes(big, hs.ENTRY_SPARSE) > hs.STATIC_SCRATCH_BYTES
+    assert hs.workspace_bytes(big, hs.ENTRY_SPARSE_STATIC) > hs.STATIC_SCRATCH_BYTES
     _expect(hs.ERR_TOO_LARGE, hs.hsa_sparse_attn_static, big, *([FAKE] * 9), stream=0)
-    for name in ("wan1.3b-480p", "wan14b-720p-90s"):
-        import synth
-        s = synth.shape(name)
-        d = hs.make_dims(H=s.H, d=s.d, Lq=s.Lq, tokens_per_frame=s.tokens_per_frame, Psize=s.Psize,
-                         P=s.P, Kp=s.Kp, Binter=s.Binter, Bintra=s.Bintra, Bq=s.Bq, r=s.r,
-                         dtype=s.dtype)
-        assert hs.workspace_bytes(d, hs.ENTRY_SPARSE) <= hs.STATIC_SCRATCH_BYTES
+    d13, d720 = (_shape_dims(n) for n in ("wan1.3b-480p", "wan14b-720p-90s"))
+    for d in (d13, d720):
+        assert hs.workspace_bytes(d, hs.ENTRY_SPARSE_STATIC) <= hs.STATIC_SCRATCH_BYTES
+    # 1.3B 480p: one split range per work-group on both entry points; the
+    # 720p 40-head shape gives hsa_sparse_attn five ranges per work-group
+    # (more partials) while the allocation-free entry keeps one
+    assert hs.workspace_bytes(d13, hs.ENTRY_SPARSE) == hs.workspace_bytes(d13, hs.ENTRY_SPARSE_STATIC)
+    assert hs.workspace_bytes(d720, hs.ENTRY_SPARSE) > hs.workspace_bytes(d720, hs.ENTRY_SPARSE_STATIC)
     assert hs._lib.hsakv_last_hip_error() == 0
 
 
