@@ -2,7 +2,9 @@
 workspace entry point hsa_sparse_attn, through the C ABI, on the same inputs:
 the results are equal bit for bit. Calls follow one another on one GPU, the
 later ones on smaller inputs, so each runs over the scratch contents its
-predecessor left behind."""
+predecessor left behind. Where the workspace entry gives each work-group
+several split ranges (more than 8 heads, more than 1024 tiles per group),
+the allocation-free entry keeps one: both are then compared with the oracle."""
 
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 import synth  # noqa: E402
 from block_sparse_rank_amd import hsakv as hs  # noqa: E402
-from gpu_util import Case, host  # noqa: E402
+from gpu_util import Case, compare, dev, host, pack_selection  # noqa: E402
 
 
 def _both(c):
@@ -42,6 +44,30 @@ def test_static_scratch_equals_workspace_entry_on_shrinking_inputs():
         ref, got = _both(Case(s))
         assert np.all(np.isfinite(got))
         assert ref.tobytes() == got.tobytes(), s.name
+
+
+def test_static_one_range_and_workspace_two_ranges_both_match_the_oracle():
+    # nine heads, 1032 tiles per group: hsa_sparse_attn runs two split ranges
+    # per work-group, hsa_sparse_attn_static one (its partials stay in scratch)
+    s = synth.shape("tiny").with_(dtype="bf16", H=9, d=64, Lq=512, tokens_per_frame=2048, Kp=4, P=6,
+                                  Binter=64, r=64, clustered=True, tau_law="uniform", seed=35)
+    d = _dims(s)
+    assert hs.workspace_bytes(d, hs.ENTRY_SPARSE) > hs.workspace_bytes(d, hs.ENTRY_SPARSE_STATIC)
+    assert hs.workspace_bytes(d, hs.ENTRY_SPARSE_STATIC) <= hs.STATIC_SCRATCH_BYTES
+    print(f"[static] {s.name} bf16 H={s.H} Lq={s.Lq} Kp={s.Kp} Tp={s.Tp}", flush=True)
+    c = Case(s)
+    ref = c.oracle()
+    _, n_sel, k_hist, v_hist = c.gather(c.page_summary())
+    cnt, idx = (dev(x) for x in pack_selection(ref["sel"], c.d.NB_max))
+    o_ws = host(c.sparse(k_hist, v_hist, n_sel, cnt, idx))
+    o_st = torch.full((s.Lq, s.H, s.d), float("nan"), dtype=torch.float32, device="cuda")
+    hs.hsa_sparse_attn_static(c.d, c.t["q"], k_hist, v_hist, c.t["k_intra"], c.t["v_intra"], n_sel,
+                              cnt, idx, o_st)
+    torch.cuda.synchronize()
+    o_st = host(o_st)
+    assert np.all(np.isfinite(o_st))
+    compare("o_sparse(workspace entry, two ranges)", o_ws, ref["o_sparse"], s.dtype)
+    compare("o_sparse(static entry, one range)", o_st, ref["o_sparse"], s.dtype)
 
 
 def _dims(s):
